@@ -41,7 +41,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["HeadConfig", "CONFIGS", "make", "make_lowrank_set", "make_hidden",
+__all__ = ["HeadConfig", "CONFIGS", "make", "make_custom", "make_lowrank_set", "make_hidden",
            "bf16_bits_to_f32", "CHUNK_ROWS"]
 
 CHUNK_ROWS = 8192
@@ -186,3 +186,19 @@ def make_lowrank_set(cid: int, set_id: int, *, B: int | None = None) -> dict:
     Pt = _round_to_dtype(_normal(sp, (cfg.V, cfg.r), std), cfg.dtype)
     H, _ = make_hidden(cfg, sh, st, B)
     return {"cfg": cfg, "Q": Qt, "P": Pt, "H": H}
+
+
+def make_custom(V: int, d: int, r: int, B: int, dtype: str = "bf16", *, seed: int = 0,
+                rows: str = "iid", e_scale: float = 0.1) -> dict:
+    """Inputs of the same recipe at arbitrary shapes (ragged and edge cases).
+
+    Seeded from SeedSequence([2000, seed, V, d, r, B]); k is left to the caller.
+    """
+    cfg = HeadConfig(0, "custom", B, d, V, r, min(64, V), dtype, rows)
+    sq, sp, se, sh, st = np.random.SeedSequence([2000, seed, V, d, r, B]).spawn(5)
+    std = 1.0 / math.sqrt(d)
+    Qt = _round_to_dtype(_normal(sq, (r, d), std), dtype)
+    Pt = _round_to_dtype(_normal(sp, (V, r), std), dtype)
+    W = _make_W(Pt, Qt, se, cfg, e_scale)
+    H, parents = make_hidden(cfg, sh, st, B)
+    return {"cfg": cfg, "Q": Qt, "P": Pt, "W": W, "H": H, "parents": parents}

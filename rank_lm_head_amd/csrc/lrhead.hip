@@ -1,0 +1,267 @@
+// lrhead.hip — host side of the C ABI in include/lrhead.h.
+//
+// Every entry point validates its arguments on the host before it touches
+// HIP, then enqueues the stage kernels on the caller's stream and returns.
+// Nothing here allocates device memory or synchronises: the caller's
+// workspace holds z and the per-slice candidate lists.
+#include "lrhead.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "launch.h"
+
+struct lrhead_s {
+  uint32_t magic;
+  int dtype;
+  int64_t V, d, r, B_max;
+  int k_max;
+  const void* Q;
+  const void* P;
+  const void* W;
+  char* ws;
+  size_t ws_bytes;
+  void* z;          // B_max x r, weight dtype
+  float* part_s;    // candidate lists: rows x slices x k_max
+  int* part_i;
+};
+
+namespace {
+
+constexpr uint32_t kMagic = 0x4c524844u;  // "LRHD"
+constexpr int64_t kBMaxLimit = int64_t(1) << 20;
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(LRHEAD_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+size_t elem_bytes(int dtype) { return dtype == LRHEAD_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  size_t z, part_s, part_i, total;
+};
+
+// Most candidate-list rows any call with B <= B_max writes (B x slices).
+int64_t max_list_rows(int64_t B_max, int64_t V) {
+  int64_t best = 0;
+  for (int64_t B = 1; B <= B_max; ++B) {
+    const int64_t rows = B * lrh::plan_vsplit(B, V);
+    if (rows > best) best = rows;
+  }
+  return best;
+}
+
+Layout layout(int dtype, int64_t V, int64_t r, int64_t B_max, int k_max) {
+  Layout L;
+  L.z = 0;
+  const size_t zb = align256(size_t(B_max) * size_t(r) * elem_bytes(dtype));
+  const size_t lists = align256(size_t(max_list_rows(B_max, V)) * size_t(k_max) * 4);
+  L.part_s = zb;
+  L.part_i = zb + lists;
+  L.total = zb + 2 * lists;
+  return L;
+}
+
+int check_shapes(int dtype, int64_t V, int64_t d, int64_t r, int64_t B_max, int k_max) {
+  if (dtype != LRHEAD_BF16 && dtype != LRHEAD_FP32) return fail(LRHEAD_EDTYPE, "unknown dtype %d", dtype);
+  if (V < 1 || V > INT32_MAX) return fail(LRHEAD_ERANGE, "V = %lld outside [1, 2^31)", (long long)V);
+  if (d < 8 || d > LRHEAD_D_MAX || d % 8) return fail(LRHEAD_ERANGE, "d = %lld: need a multiple of 8 in [8, %d]", (long long)d, LRHEAD_D_MAX);
+  if (r < 8 || r > LRHEAD_R_MAX || r % 8) return fail(LRHEAD_ERANGE, "r = %lld: need a multiple of 8 in [8, %d]", (long long)r, LRHEAD_R_MAX);
+  if (B_max < 1 || B_max > kBMaxLimit) return fail(LRHEAD_ERANGE, "B_max = %lld outside [1, 2^20]", (long long)B_max);
+  if (k_max < 1 || k_max > LRHEAD_K_MAX || k_max > V)
+    return fail(LRHEAD_ERANGE, "k_max = %d outside [1, min(%d, V)]", k_max, LRHEAD_K_MAX);
+  return LRHEAD_OK;
+}
+
+int check_handle(const lrhead_s* h) {
+  if (!h || h->magic != kMagic) return fail(LRHEAD_EINVAL, "invalid handle");
+  return LRHEAD_OK;
+}
+
+int check_rows(const lrhead_s* h, const void* H, int64_t B) {
+  if (B < 0 || B > h->B_max) return fail(LRHEAD_ERANGE, "B = %lld outside [0, B_max = %lld]", (long long)B, (long long)h->B_max);
+  if (B > 0 && !H) return fail(LRHEAD_EINVAL, "H is NULL");
+  if (!aligned16(H)) return fail(LRHEAD_EALIGN, "H is not 16-byte aligned");
+  return LRHEAD_OK;
+}
+
+int check_k(const lrhead_s* h, int k) {
+  if (k < 1 || k > h->k_max) return fail(LRHEAD_ERANGE, "k = %d outside [1, k_max = %d]", k, h->k_max);
+  return LRHEAD_OK;
+}
+
+int check_out(const void* p, const char* name, bool required) {
+  if (!p) return required ? fail(LRHEAD_EINVAL, "%s is NULL", name) : LRHEAD_OK;
+  if (!aligned16(p)) return fail(LRHEAD_EALIGN, "%s is not 16-byte aligned", name);
+  return LRHEAD_OK;
+}
+
+#define LRH_TRY(x)            \
+  do {                        \
+    const int rc_ = (x);      \
+    if (rc_ != LRHEAD_OK) return rc_; \
+  } while (0)
+
+#define LRH_HIP(x, what)                 \
+  do {                                   \
+    const hipError_t e_ = (x);           \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+int enqueue_candidates(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, float* score,
+                       hipStream_t s) {
+  LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
+  const int nvs = lrh::plan_vsplit(B, h->V);
+  LRH_HIP(lrh::launch_select(h->dtype, h->P, h->z, h->V, (int)h->r, B, k, nvs, h->part_s, h->part_i, s),
+          "score/selection launch");
+  LRH_HIP(lrh::launch_merge(h->part_s, h->part_i, nvs, B, k, idx, score, s), "merge launch");
+  return LRHEAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lrhead_workspace_bytes(int dtype, int64_t V, int64_t d, int64_t r, int64_t B_max, int k_max) {
+  if (check_shapes(dtype, V, d, r, B_max, k_max) != LRHEAD_OK) return 0;
+  return layout(dtype, V, r, B_max, k_max).total;
+}
+
+int lrhead_create(lrhead_t* out, int dtype, int64_t V, int64_t d, int64_t r, const void* Q, const void* P,
+                  const void* W, int64_t B_max, int k_max, void* workspace, size_t workspace_bytes) {
+  if (!out) return fail(LRHEAD_EINVAL, "out is NULL");
+  *out = nullptr;
+  LRH_TRY(check_shapes(dtype, V, d, r, B_max, k_max));
+  if (!Q || !P || !W) return fail(LRHEAD_EINVAL, "Q, P and W must be non-NULL");
+  if (!workspace) return fail(LRHEAD_EINVAL, "workspace is NULL");
+  if (!aligned16(Q) || !aligned16(P) || !aligned16(W) || !aligned16(workspace))
+    return fail(LRHEAD_EALIGN, "Q, P, W and workspace must be 16-byte aligned");
+  const Layout L = layout(dtype, V, r, B_max, k_max);
+  if (workspace_bytes < L.total)
+    return fail(LRHEAD_EWORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, L.total);
+
+  int dev = 0;
+  LRH_HIP(hipGetDevice(&dev), "hipGetDevice");
+  hipDeviceProp_t prop;
+  LRH_HIP(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(LRHEAD_EDEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+
+  lrhead_s* h = new (std::nothrow) lrhead_s;
+  if (!h) return fail(LRHEAD_EINVAL, "out of host memory");
+  h->magic = kMagic;
+  h->dtype = dtype;
+  h->V = V;
+  h->d = d;
+  h->r = r;
+  h->B_max = B_max;
+  h->k_max = k_max;
+  h->Q = Q;
+  h->P = P;
+  h->W = W;
+  h->ws = static_cast<char*>(workspace);
+  h->ws_bytes = workspace_bytes;
+  h->z = h->ws + L.z;
+  h->part_s = reinterpret_cast<float*>(h->ws + L.part_s);
+  h->part_i = reinterpret_cast<int*>(h->ws + L.part_i);
+  *out = h;
+  return LRHEAD_OK;
+}
+
+int lrhead_candidates(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, float* score, void* stream) {
+  LRH_TRY(check_handle(h));
+  LRH_TRY(check_rows(h, H, B));
+  LRH_TRY(check_k(h, k));
+  LRH_TRY(check_out(idx, "idx", B > 0));
+  LRH_TRY(check_out(score, "score", false));
+  if (B == 0) return LRHEAD_OK;
+  return enqueue_candidates(h, H, B, k, idx, score, static_cast<hipStream_t>(stream));
+}
+
+int fullhead_logits(lrhead_t h, const void* H, int64_t B, const int32_t* idx, int k, float* logits,
+                    void* stream) {
+  LRH_TRY(check_handle(h));
+  LRH_TRY(check_rows(h, H, B));
+  LRH_TRY(check_out(idx, "idx", false));
+  if (idx) LRH_TRY(check_k(h, k));
+  LRH_TRY(check_out(logits, "logits", B > 0));
+  if (B == 0) return LRHEAD_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!idx) {
+    LRH_HIP(lrh::launch_dense(h->dtype, h->W, H, h->V, (int)h->d, B, logits, s), "dense logits launch");
+    return LRHEAD_OK;
+  }
+  LRH_HIP(lrh::launch_rescore(h->dtype, h->W, H, idx, B, k, h->V, (int)h->d, logits, s), "rescore launch");
+  return LRHEAD_OK;
+}
+
+int fullhead_topk(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, float* logits, void* stream) {
+  LRH_TRY(check_handle(h));
+  LRH_TRY(check_rows(h, H, B));
+  LRH_TRY(check_k(h, k));
+  LRH_TRY(check_out(idx, "idx", B > 0));
+  LRH_TRY(check_out(logits, "logits", B > 0));
+  if (B == 0) return LRHEAD_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nvs = lrh::plan_vsplit(B, h->V);
+  LRH_HIP(lrh::launch_select(h->dtype, h->W, H, h->V, (int)h->d, B, k, nvs, h->part_s, h->part_i, s),
+          "full-head selection launch");
+  LRH_HIP(lrh::launch_merge(h->part_s, h->part_i, nvs, B, k, idx, logits, s), "merge launch");
+  return LRHEAD_OK;
+}
+
+int lrhead_draft(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, float* score, float* logits,
+                 void* stream) {
+  LRH_TRY(check_handle(h));
+  LRH_TRY(check_rows(h, H, B));
+  LRH_TRY(check_k(h, k));
+  LRH_TRY(check_out(idx, "idx", B > 0));
+  LRH_TRY(check_out(score, "score", false));
+  LRH_TRY(check_out(logits, "logits", B > 0));
+  if (B == 0) return LRHEAD_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  LRH_TRY(enqueue_candidates(h, H, B, k, idx, score, s));
+  LRH_HIP(lrh::launch_rescore(h->dtype, h->W, H, idx, B, k, h->V, (int)h->d, logits, s), "rescore launch");
+  return LRHEAD_OK;
+}
+
+void lrhead_destroy(lrhead_t h) {
+  if (h && h->magic == kMagic) {
+    h->magic = 0;
+    delete h;
+  }
+}
+
+const char* lrhead_strerror(int code) {
+  switch (code) {
+    case LRHEAD_OK: return "success";
+    case LRHEAD_EINVAL: return "invalid argument";
+    case LRHEAD_ERANGE: return "size outside the supported range";
+    case LRHEAD_EDTYPE: return "unknown dtype";
+    case LRHEAD_EALIGN: return "pointer not 16-byte aligned";
+    case LRHEAD_EWORKSPACE: return "workspace too small";
+    case LRHEAD_EHIP: return "HIP error";
+    case LRHEAD_EDEVICE: return "device is not gfx950";
+    default: return "unknown error code";
+  }
+}
+
+const char* lrhead_last_error(void) { return g_err; }
+
+}  // extern "C"

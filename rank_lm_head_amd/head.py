@@ -1,0 +1,142 @@
+"""Python binding of the low-rank draft LM head (argument marshalling only).
+
+Every step of the head runs in liblrhead.so's HIP kernels; this module checks
+tensor dtypes, devices and shapes, hands raw device pointers and torch's
+current HIP stream to the C ABI, and allocates outputs and the workspace with
+torch. See include/lrhead.h for the operations and their contracts.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.bfloat16: _lib.BF16, torch.float32: _lib.FP32}
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+class Head:
+    """A low-rank head (Q: r x d, P: V x r) with its full-rank head W (V x d).
+
+    The tensors must live on one ROCm device, share dtype (bfloat16 or
+    float32) and be contiguous; they are borrowed, not copied.
+    """
+
+    def __init__(self, Q: torch.Tensor, P: torch.Tensor, W: torch.Tensor, *,
+                 B_max: int, k_max: int, workspace: torch.Tensor | None = None):
+        _need(Q.dtype in _DTYPES, f"unsupported dtype {Q.dtype}")
+        _need(P.dtype == Q.dtype and W.dtype == Q.dtype, "Q, P, W must share a dtype")
+        _need(Q.dim() == 2 and P.dim() == 2 and W.dim() == 2, "Q, P, W must be matrices")
+        r, d = Q.shape
+        V = P.shape[0]
+        _need(tuple(P.shape) == (V, r), f"P is {tuple(P.shape)}, expected ({V}, {r})")
+        _need(tuple(W.shape) == (V, d), f"W is {tuple(W.shape)}, expected ({V}, {d})")
+        for name, t in (("Q", Q), ("P", P), ("W", W)):
+            _need(t.is_cuda and t.device == Q.device, f"{name} must be on {Q.device}")
+            _need(t.is_contiguous(), f"{name} must be contiguous")
+        self.lib = _lib.load()
+        self.dtype = Q.dtype
+        self.code = _DTYPES[Q.dtype]
+        self.device = Q.device
+        self.V, self.d, self.r = int(V), int(d), int(r)
+        self.B_max, self.k_max = int(B_max), int(k_max)
+        nbytes = self.lib.lrhead_workspace_bytes(self.code, V, d, r, B_max, k_max)
+        if nbytes == 0:
+            _lib.check(self.lib.lrhead_create(ctypes.byref(ctypes.c_void_p()), self.code, V, d, r,
+                                              None, None, None, B_max, k_max, None, 0),
+                       "lrhead_workspace_bytes")
+        if workspace is None:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        _need(workspace.dtype == torch.uint8 and workspace.is_cuda and workspace.numel() >= nbytes,
+              f"workspace must be a uint8 device tensor of >= {nbytes} bytes")
+        self.workspace = workspace
+        self._tensors = (Q, P, W)
+        self._h = ctypes.c_void_p()
+        rc = self.lib.lrhead_create(ctypes.byref(self._h), self.code, V, d, r, _ptr(Q), _ptr(P), _ptr(W),
+                                    B_max, k_max, _ptr(workspace), workspace.numel())
+        _lib.check(rc, "lrhead_create")
+
+    # ------------------------------------------------------------ helpers
+    def _stream(self):
+        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+
+    def _rows(self, H: torch.Tensor) -> int:
+        _need(H.dtype == self.dtype, f"H must be {self.dtype}")
+        _need(H.dim() == 2 and H.shape[1] == self.d, f"H must be (B, {self.d})")
+        _need(H.is_cuda and H.device == self.device and H.is_contiguous(), "H must be contiguous on the device")
+        return int(H.shape[0])
+
+    def _out(self, shape, dtype):
+        return torch.empty(shape, dtype=dtype, device=self.device)
+
+    # -------------------------------------------------------------- calls
+    def candidates(self, H: torch.Tensor, k: int, *, want_score: bool = True):
+        """Low-rank retrieval: (idx int32 [B, k], score fp32 [B, k] or None)."""
+        B = self._rows(H)
+        idx = self._out((B, k), torch.int32)
+        score = self._out((B, k), torch.float32) if want_score else None
+        _lib.check(self.lib.lrhead_candidates(self._h, _ptr(H), B, k, _ptr(idx), _ptr(score), self._stream()),
+                   "lrhead_candidates")
+        return idx, score
+
+    def logits(self, H: torch.Tensor, idx: torch.Tensor) -> torch.Tensor:
+        """Exact full-rank logits of the given ids (fp32 [B, k])."""
+        B = self._rows(H)
+        _need(idx.dtype == torch.int32 and idx.dim() == 2 and idx.shape[0] == B, "idx must be int32 (B, k)")
+        _need(idx.is_cuda and idx.is_contiguous(), "idx must be contiguous on the device")
+        k = int(idx.shape[1])
+        out = self._out((B, k), torch.float32)
+        _lib.check(self.lib.fullhead_logits(self._h, _ptr(H), B, _ptr(idx), k, _ptr(out), self._stream()),
+                   "fullhead_logits")
+        return out
+
+    def dense_logits(self, H: torch.Tensor) -> torch.Tensor:
+        """All V full-head logits (fp32 [B, V]); a test aid."""
+        B = self._rows(H)
+        out = self._out((B, self.V), torch.float32)
+        _lib.check(self.lib.fullhead_logits(self._h, _ptr(H), B, None, 0, _ptr(out), self._stream()),
+                   "fullhead_logits(dense)")
+        return out
+
+    def full_topk(self, H: torch.Tensor, k: int):
+        """Full-head baseline: (idx int32 [B, k], logits fp32 [B, k])."""
+        B = self._rows(H)
+        idx = self._out((B, k), torch.int32)
+        logits = self._out((B, k), torch.float32)
+        _lib.check(self.lib.fullhead_topk(self._h, _ptr(H), B, k, _ptr(idx), _ptr(logits), self._stream()),
+                   "fullhead_topk")
+        return idx, logits
+
+    def draft(self, H: torch.Tensor, k: int, *, want_score: bool = True, out=None):
+        """One draft-head call: (idx, score or None, logits), all [B, k]."""
+        B = self._rows(H)
+        if out is None:
+            idx = self._out((B, k), torch.int32)
+            score = self._out((B, k), torch.float32) if want_score else None
+            logits = self._out((B, k), torch.float32)
+        else:
+            idx, score, logits = out
+        _lib.check(self.lib.lrhead_draft(self._h, _ptr(H), B, k, _ptr(idx), _ptr(score), _ptr(logits),
+                                         self._stream()), "lrhead_draft")
+        return idx, score, logits
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self.lib.lrhead_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,217 @@
+"""GPU parity of the HIP head against the float64 oracle, through the C ABI.
+
+Rule (oracle/compare.py): candidate ids bit-exact as a set wherever the
+oracle's k-th/(k+1)-th gap exceeds 1e-3 * max|score|, boundary swaps only
+inside that band; logits within 2e-3 (bf16) or 1e-5 (fp32) relative.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import rank_lm_head_amd as lr
+from parity_util import check_full, check_lowrank, check_properties, dev
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def np_(t):
+    return None if t is None else t.cpu().numpy()
+
+
+@functools.lru_cache(maxsize=1)
+def config(cid: int):
+    say(f"[gen] config {cid}")
+    inp = gen.make(cid)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    return inp, t
+
+
+def head_for(inp, t, B_max=None, k_max=None):
+    cfg = inp["cfg"]
+    return lr.Head(t["Q"], t["P"], t["W"], B_max=B_max or cfg.B, k_max=k_max or cfg.k)
+
+
+# ------------------------------------------------------------ tiny fp32 head
+
+def test_tiny_fp32_every_call():
+    inp, t = config(1)
+    k = inp["cfg"].k
+    head = head_for(inp, t)
+    say("[run] c1 candidates / logits / draft / full_topk / dense")
+    idx, score = head.candidates(t["H"], k)
+    lg = head.logits(t["H"], idx)
+    didx, dscore, dlg = head.draft(t["H"], k)
+    fidx, flog = head.full_topk(t["H"], k)
+    dense = head.dense_logits(t["H"])
+    torch.cuda.synchronize()
+    idx, score, lg = np_(idx), np_(score), np_(lg)
+    errs, stats = check_lowrank(inp, k, idx, score, lg)
+    assert not errs, errs
+    assert np.array_equal(np_(didx), idx) and np.array_equal(np_(dlg), lg)
+    assert np.array_equal(np_(dscore), score)
+    errs, _ = check_full(inp, k, np_(fidx), np_(flog))
+    assert not errs, errs
+    L = oracle.full_head(inp["W"], inp["H"], k, "fp32", keep_logits=True)["L"]
+    dn = np_(dense)
+    # a priori bound of an fp32 dot product of length d: d * 2^-24 * sum |w_i h_i|
+    absdot = np.abs(oracle.to_f64(inp["W"], "fp32")) @ np.abs(oracle.to_f64(inp["H"], "fp32")[0])
+    assert np.all(np.abs(dn[0] - L[0]) <= inp["cfg"].d * 2.0 ** -24 * absdot)
+    say(f"[ok] c1 {stats}")
+
+
+# ----------------------------------------------- small heads: tiles and tails
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("V,d,r,B,k", [
+    (1000, 136, 40, 19, 7),      # ragged vocabulary tile, k tail in both contractions, ragged rows
+    (4099, 264, 24, 33, 64),     # k = 64, three row tiles, V % 16 == 3
+    (17, 64, 16, 2, 17),         # k = V
+    (10, 32, 8, 1, 1),           # V below one tile
+    (2500, 512, 512, 5, 33),     # r at its maximum
+])
+def test_small_heads(dt, V, d, r, B, k):
+    inp = gen.make_custom(V, d, r, B, dt, seed=V + d)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=k)
+    say(f"[run] small {dt} V={V} d={d} r={r} B={B} k={k}")
+    idx, score, lg = head.draft(t["H"], k)
+    fidx, flog = head.full_topk(t["H"], k)
+    torch.cuda.synchronize()
+    errs, stats = check_lowrank(inp, k, np_(idx), np_(score), np_(lg))
+    assert not errs, errs[:5]
+    errs, _ = check_full(inp, k, np_(fidx), np_(flog))
+    assert not errs, errs[:5]
+    say(f"[ok] {stats}")
+
+
+def test_empty_batch_is_a_noop():
+    inp = gen.make_custom(300, 64, 16, 4, "bf16", seed=1)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=4, k_max=8)
+    idx, score, lg = head.draft(t["H"][:0], 8)
+    assert idx.shape == (0, 8) and lg.shape == (0, 8)
+    fidx, flog = head.full_topk(t["H"][:0], 8)
+    torch.cuda.synchronize()
+    assert fidx.numel() == 0
+
+
+def test_calls_reject_bad_arguments_on_a_real_handle():
+    inp = gen.make_custom(300, 64, 16, 4, "bf16", seed=2)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=4, k_max=8)
+    L = head.lib
+    H = t["H"]
+    out = torch.empty(64, dtype=torch.int32, device=DEV)
+    import ctypes
+    p = lambda x: ctypes.c_void_p(x.data_ptr())
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert L.lrhead_candidates(head._h, p(H), 5, 4, p(out), None, s) == lr._lib.ERANGE     # B > B_max
+    assert L.lrhead_candidates(head._h, p(H), 1, 9, p(out), None, s) == lr._lib.ERANGE     # k > k_max
+    assert L.lrhead_candidates(head._h, p(H), 1, 0, p(out), None, s) == lr._lib.ERANGE     # k < 1
+    assert L.lrhead_candidates(head._h, ctypes.c_void_p(H.data_ptr() + 2), 1, 4, p(out), None, s) == lr._lib.EALIGN
+    assert L.fullhead_topk(head._h, p(H), 1, 4, None, p(out), s) == lr._lib.EINVAL
+    assert L.fullhead_logits(head._h, p(H), 1, p(out), 9, p(out), s) == lr._lib.ERANGE
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------- the five configurations
+
+def _sample_rows(B: int) -> np.ndarray:
+    if B <= 64:
+        return np.arange(B)
+    return np.unique(np.concatenate([np.linspace(0, B - 1, 126).astype(int), [1, B - 2]]))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_config_draft_head(cid):
+    inp, t = config(cid)
+    cfg = inp["cfg"]
+    head = head_for(inp, t)
+    say(f"[run] c{cid} draft head B={cfg.B} r={cfg.r} k={cfg.k}")
+    idx, score, lg = head.draft(t["H"], cfg.k)
+    torch.cuda.synchronize()
+    idx, score, lg = np_(idx), np_(score), np_(lg)
+    assert not check_properties(idx, score, cfg.V)
+    assert np.all(np.isfinite(lg))
+    rows = _sample_rows(cfg.B)
+    errs, stats = check_lowrank(inp, cfg.k, idx, score, lg, rows=rows)
+    say(f"[ok?] c{cid} rows checked {len(rows)} {stats} errors {len(errs)}")
+    assert not errs, errs[:5]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_config_full_head_baseline(cid):
+    inp, t = config(cid)
+    cfg = inp["cfg"]
+    head = head_for(inp, t)
+    say(f"[run] c{cid} full head B={cfg.B} k={cfg.k}")
+    fidx, flog = head.full_topk(t["H"], cfg.k)
+    torch.cuda.synchronize()
+    fidx, flog = np_(fidx), np_(flog)
+    assert not check_properties(fidx, flog, cfg.V)
+    rows = _sample_rows(cfg.B)
+    errs, stats = check_full(inp, cfg.k, fidx, flog, rows=rows)
+    say(f"[ok?] c{cid} full rows checked {len(rows)} {stats} errors {len(errs)}")
+    assert not errs, errs[:5]
+
+
+# ------------------------------------------------------ invariants on the GPU
+
+def test_h_times_two_doubles_everything_bitwise():
+    inp = gen.make_custom(5000, 256, 64, 20, "bf16", seed=4)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=20, k_max=32)
+    a = [np_(x) for x in head.draft(t["H"], 32)]
+    b = [np_(x) for x in head.draft((t["H"].float() * 2).to(torch.bfloat16), 32)]
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(2 * a[1], b[1]) and np.array_equal(2 * a[2], b[2])
+
+
+def test_duplicate_rows_tie_to_the_lower_id():
+    V = 3000
+    inp = gen.make_custom(V, 128, 32, 1, "bf16", seed=5)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=1, k_max=4)
+    tok = int(np_(head.candidates(t["H"], 1)[0])[0, 0])
+    ftok = int(np_(head.full_topk(t["H"], 1)[0])[0, 0])
+    assert tok not in (0, V - 1) and ftok not in (0, V - 1)
+    P2, W2 = t["P"].clone(), t["W"].clone()
+    for dst in (0, V - 1):          # bitwise copies of the best rows, below and above
+        P2[dst] = t["P"][tok]
+        W2[dst] = t["W"][ftok]
+    h2 = lr.Head(t["Q"], P2, W2, B_max=1, k_max=4)
+    idx, score = h2.candidates(t["H"], 3)
+    assert np_(idx)[0].tolist() == [0, tok, V - 1]
+    assert len(set(np_(score)[0].tolist())) == 1
+    assert np_(h2.candidates(t["H"], 1)[0])[0, 0] == 0
+    fidx, flog = h2.full_topk(t["H"], 3)
+    assert np_(fidx)[0].tolist() == [0, ftok, V - 1]
+    assert len(set(np_(flog)[0].tolist())) == 1
+
+
+def test_repeat_calls_and_poisoned_workspace_are_bitwise_stable():
+    inp = gen.make_custom(20000, 512, 128, 40, "bf16", seed=6)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=40, k_max=64)
+    ref = [np_(x) for x in head.draft(t["H"], 64)]
+    for trial in range(5):
+        head.workspace.fill_(0xFF if trial % 2 else 0x7F)     # NaN / large garbage
+        got = [np_(x) for x in head.draft(t["H"], 64)]
+        for a, b in zip(ref, got):
+            assert np.array_equal(a, b)
+    f1 = [np_(x) for x in head.full_topk(t["H"], 64)]
+    f2 = [np_(x) for x in head.full_topk(t["H"], 64)]
+    assert all(np.array_equal(a, b) for a, b in zip(f1, f2))
