@@ -148,6 +148,16 @@ int fullhead_topk(lrhead_t h, const void* H, int64_t B, int k,
 int lrhead_draft(lrhead_t h, const void* H, int64_t B, int k,
                  int32_t* idx, float* score, float* logits, void* stream);
 
+/*
+ * Profiling aid: hipEvent_t handles (passed as void*) that later calls on
+ * this handle record on their stream immediately before and after the
+ * vocabulary score/selection kernel (lrhead_candidates, lrhead_draft,
+ * fullhead_topk), so a caller can time that kernel with hipEventElapsedTime.
+ * Pass NULL, NULL to stop. The events are borrowed; recording them is the
+ * only effect.
+ */
+int lrhead_set_stage_events(lrhead_t h, void* before, void* after);
+
 /* Releases the handle's host memory (never the borrowed device buffers). */
 void lrhead_destroy(lrhead_t h);
 

@@ -94,33 +94,66 @@ __device__ __forceinline__ f32x4 tile_dot(const float* __restrict__ a, bool a_ok
 }
 
 // ------------------------------------------------------- wave-wide ordering
-// One (score, id) pair per lane. After bitonic_sort_desc the 64 pairs are in
-// candidate order across lanes 0..63 (best first).
-__device__ __forceinline__ void cmpx(float& s, int& i, int stride, bool keep_better) {
-  const float os = __shfl_xor(s, stride);
-  const int oi = __shfl_xor(i, stride);
-  const bool other_first = precedes(os, oi, s, i);
-  if (other_first == keep_better) { s = os; i = oi; }
+// Value of lane (l ^ S). Distances up to 8 stay inside a row of 16 lanes and
+// use DPP, written only with direction-free patterns: quad permutes (1, 2),
+// the half-row mirror followed by a quad reversal (4: lane i of a half row
+// reads 7 - (3 - i) = i + 4, and the other way round), and a rotation of the
+// row by 8. Distance 16 uses ds_swizzle (xor mask 16 within 32 lanes), 32 a
+// ds_bpermute.
+template <int S>
+__device__ __forceinline__ int lane_xor(int x) {
+  if constexpr (S == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, true);
+  else if constexpr (S == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, true);
+  else if constexpr (S == 4)
+    return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, true), 0x1B, 0xf, 0xf, true);
+  else if constexpr (S == 8) return __builtin_amdgcn_mov_dpp(x, 0x128, 0xf, 0xf, true);
+  else if constexpr (S == 16) return __builtin_amdgcn_ds_swizzle(x, 0x401F);
+  else return __shfl_xor(x, 32);
 }
 
+template <int S>
+__device__ __forceinline__ void cmpx(float& s, int& i, bool keep_better) {
+  const float os = __int_as_float(lane_xor<S>(__float_as_int(s)));
+  const int oi = lane_xor<S>(i);
+  const bool other_first = precedes(os, oi, s, i);
+  if (other_first == keep_better) {
+    s = os;
+    i = oi;
+  }
+}
+
+// One merge step of a bitonic network: distance S inside blocks of SIZE.
+template <int SIZE, int S>
+__device__ __forceinline__ void bitonic_step(float& s, int& i, int lane) {
+  const bool lower = (lane & S) == 0;
+  const bool desc_block = SIZE >= kWave ? true : (lane & SIZE) == 0;
+  cmpx<S>(s, i, lower == desc_block);
+}
+
+template <int SIZE>
+__device__ __forceinline__ void bitonic_stage(float& s, int& i, int lane) {
+  if constexpr (SIZE >= 64) bitonic_step<SIZE, 32>(s, i, lane);
+  if constexpr (SIZE >= 32) bitonic_step<SIZE, 16>(s, i, lane);
+  if constexpr (SIZE >= 16) bitonic_step<SIZE, 8>(s, i, lane);
+  if constexpr (SIZE >= 8) bitonic_step<SIZE, 4>(s, i, lane);
+  if constexpr (SIZE >= 4) bitonic_step<SIZE, 2>(s, i, lane);
+  bitonic_step<SIZE, 1>(s, i, lane);
+}
+
+// Sorts the wave's 64 pairs into candidate order (best in lane 0).
 __device__ __forceinline__ void bitonic_sort_desc(float& s, int& i) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const bool lower = (lane & stride) == 0;
-      const bool desc_block = (lane & size) == 0;
-      cmpx(s, i, stride, lower == desc_block);
-    }
-  }
+  bitonic_stage<2>(s, i, lane);
+  bitonic_stage<4>(s, i, lane);
+  bitonic_stage<8>(s, i, lane);
+  bitonic_stage<16>(s, i, lane);
+  bitonic_stage<32>(s, i, lane);
+  bitonic_stage<64>(s, i, lane);
 }
 
 // Sorts a bitonic sequence of 64 pairs into candidate order.
 __device__ __forceinline__ void bitonic_merge_desc(float& s, int& i) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int stride = kWave >> 1; stride > 0; stride >>= 1) cmpx(s, i, stride, (lane & stride) == 0);
+  bitonic_stage<64>(s, i, threadIdx.x & 63);
 }
 
 // (s, i) is sorted (best first) across the wave and (ts, ti) holds another
@@ -129,6 +162,74 @@ __device__ __forceinline__ void bitonic_merge_desc(float& s, int& i) {
 __device__ __forceinline__ void merge_reversed(float& s, int& i, float ts, int ti) {
   if (precedes(ts, ti, s, i)) { s = ts; i = ti; }
   bitonic_merge_desc(s, i);
+}
+
+// ------------------------------------------------------------ lane groups
+// Sum over aligned groups of N lanes (N a power of two <= 64); every lane of
+// a group receives the group's sum. N <= 16 uses DPP within a row of 16
+// lanes: quad permutes for distances 1 and 2, then the half-row and row
+// mirrors (lane i with 7-i, and with 15-i), which pair lanes whose partial
+// sums already cover disjoint halves.
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), Ctrl, 0xf, 0xf, true));
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "group size");
+  if constexpr (N >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp<0x141>(x);   // row_half_mirror
+  if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Dot product of 8 bf16 pairs (two 16-byte chunks) with fp32 accumulation.
+// Each bf16 is widened exactly (it is the top half of an fp32 word) and the
+// products are accumulated with fp32 FMAs in element order.
+__device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = fmaf(__uint_as_float(a[q] << 16), __uint_as_float(b[q] << 16), acc);
+    acc = fmaf(__uint_as_float(a[q] & 0xffff0000u), __uint_as_float(b[q] & 0xffff0000u), acc);
+  }
+  return acc;
+}
+
+// 8 bf16 widened to fp32, in element order.
+struct f32x8 {
+  float v[8];
+};
+__device__ __forceinline__ f32x8 widen8(u32x4 a) {
+  f32x8 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    r.v[2 * q] = __uint_as_float(a[q] << 16);
+    r.v[2 * q + 1] = __uint_as_float(a[q] & 0xffff0000u);
+  }
+  return r;
+}
+
+// Same sum as dot8_bf16 with the second operand already widened.
+__device__ __forceinline__ float dot8_bf16(u32x4 a, const f32x8& b, float acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = fmaf(__uint_as_float(a[q] << 16), b.v[2 * q], acc);
+    acc = fmaf(__uint_as_float(a[q] & 0xffff0000u), b.v[2 * q + 1], acc);
+  }
+  return acc;
+}
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
 }  // namespace lrh

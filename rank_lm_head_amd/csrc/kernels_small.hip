@@ -1,0 +1,351 @@
+// kernels_small.hip — the head for a few draft rows (B <= 4), bf16.
+//
+// With one to four rows both contractions are matrix-vector products and
+// the time is HBM streaming ("EAGLE-4", section "Retrieve vocabulary
+// candidates cheaply, then score them exactly": the low-rank head still
+// scores every vocabulary row, so P is read once per call). Matrix cores
+// would leave 15 of their 16 columns idle here, so these kernels use the
+// vector ALU (bf16 widened to fp32, fp32 FMAs) and spend their effort on
+// the memory side: every wave load is 64 lanes x 16 contiguous bytes, and
+// each wave keeps several loads in flight.
+//
+//   down_small_kernel   z = Q . h: one wave per row of Q
+//   select_short_kernel s = P . z with the fused k-best of each block's
+//                       slice, for r <= 512 (a power of two)
+//   select_long_kernel  the same for rows longer than one wave load (the
+//                       full-head baseline, W . h)
+// The slice lists are merged, and the winners rescored, by merge_kernel.
+#include "launch.h"
+#include "topk.h"
+
+namespace lrh {
+
+constexpr int kWavesSmall = 4;
+constexpr int kSmallThreads = kWavesSmall * kWave;
+
+// ------------------------------------------------------------ z = Q . h
+// Wave w of block x computes z[b][j] for j = 4x + w and every row b < B.
+// A row of Q is NL wave loads of 1 KiB (d <= NL * 512); all of them and the
+// matching chunks of h are issued before the products. Loads past d read a
+// clamped, valid address and are zeroed afterwards, so no load is predicated.
+template <int NB, int NL>
+__global__ void __launch_bounds__(kSmallThreads) down_small_kernel(const uint16_t* __restrict__ Q,
+                                                                   const uint16_t* __restrict__ H, int r,
+                                                                   int d, int B, uint16_t* __restrict__ Z) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = blockIdx.x * kWavesSmall + wave;
+  if (j >= r) return;
+  const uint16_t* q = Q + (int64_t)j * d;
+  u32x4 qv[NL], hv[NB][NL];
+#pragma unroll
+  for (int t = 0; t < NL; ++t) {
+    const int c = (t * kWave + lane) * 8;
+    const int cc = c < d ? c : d - 8;
+    qv[t] = load16(q + cc);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) hv[b][t] = load16(H + (int64_t)(b < B ? b : 0) * d + cc);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      const bool ok = (t * kWave + lane) * 8 < d;
+      acc = dot8_bf16(ok ? qv[t] : u32x4{0u, 0u, 0u, 0u}, hv[b][t], acc);
+    }
+    const float z = group_sum<kWave>(acc);
+    if (b < B && lane == 0) Z[(int64_t)b * r + j] = f32_to_bf16(z);
+  }
+}
+
+// ------------------------------------------------- shared tail of the pass
+// Each wave hands its per-row lists to LDS; wave b merges the four lists of
+// row b and writes the block's sorted list to part_[b][block][0..k).
+template <int NB>
+struct SmallLds {
+  float bs[kWavesSmall][NB][kBuf];
+  int bi[kWavesSmall][NB][kBuf];
+  float cs[kWavesSmall][NB][kWave];
+  int ci[kWavesSmall][NB][kWave];
+};
+
+template <int NB>
+__device__ __forceinline__ void finish_block(SmallLds<NB>& sm, WaveSel<NB>& st, int B, int k,
+                                             float* __restrict__ part_s, int* __restrict__ part_i) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nblk = gridDim.x;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b >= B) break;
+    if (st.cnt[b] > 0) st.fold(b, sm.bs[wave][b], sm.bi[wave][b], k);
+    sm.cs[wave][b][lane] = st.ls[b];
+    sm.ci[wave][b][lane] = st.li[b];
+  }
+  __syncthreads();
+  if (wave < B) {
+    const int b = wave;
+    float s = sm.cs[0][b][lane];
+    int i = sm.ci[0][b][lane];
+#pragma unroll
+    for (int w = 1; w < kWavesSmall; ++w)
+      merge_reversed(s, i, sm.cs[w][b][kWave - 1 - lane], sm.ci[w][b][kWave - 1 - lane]);
+    if (lane < k) {
+      const int64_t o = ((int64_t)b * nblk + blockIdx.x) * k + lane;
+      part_s[o] = s;
+      part_i[o] = i;
+    }
+  }
+}
+
+// ------------------------------------------- score pass, rows <= 512 long
+// K/8 lanes hold one vocabulary row (16 bytes each), so one wave load is 1
+// KiB of consecutive rows. Block x owns the contiguous slice
+// [V*x/n, V*(x+1)/n) (at most kBlockRows rows) and each wave a quarter of
+// it; the next U wave loads are issued before the current ones are used.
+// The scores go to LDS, and after the pass wave b finds the k best of the
+// slice for row b by bisection (topk.h) and writes them, in order, to
+// part_[b][x][0..k).
+constexpr int kBlockRows = 512;
+
+template <int K, int NB, int E>
+__global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
+    const uint16_t* __restrict__ M, const uint16_t* __restrict__ X, int64_t V, int B, int k,
+    float* __restrict__ part_s, int* __restrict__ part_i) {
+  constexpr int LPR = K / 8;
+  constexpr int RPL = kWave / LPR;
+  constexpr int U = 8;
+  constexpr int STEP = U * RPL;
+  static_assert(K % 8 == 0 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "row length");
+  __shared__ float sc[NB][E * kWave];
+  __shared__ uint64_t tmp[NB][kWave];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane % LPR, sub = lane / LPR;
+
+  f32x8 zc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) zc[b] = widen8(b < B ? load16(X + (int64_t)b * K + 8 * c) : u32x4{0u, 0u, 0u, 0u});
+
+  const int64_t nblk = gridDim.x;
+  const int64_t blo = V * blockIdx.x / nblk, bhi = V * (blockIdx.x + 1) / nblk;
+  const int64_t wlo = blo + (bhi - blo) * wave / kWavesSmall;
+  const int64_t whi = blo + (bhi - blo) * (wave + 1) / kWavesSmall;
+
+  // Rows past the wave's range are loaded from its last row (a valid
+  // address, so no load is predicated) and never kept.
+  const int64_t last = whi - 1;
+  u32x4 cur[U], nxt[U];
+  if (wlo < whi) {
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int64_t row = wlo + t * RPL + sub;
+      cur[t] = load16(M + (row < last ? row : last) * K + 8 * c);
+    }
+  }
+  for (int64_t base = wlo; base < whi; base += STEP) {
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int64_t row = base + STEP + t * RPL + sub;
+      nxt[t] = load16(M + (row < last ? row : last) * K + 8 * c);
+    }
+#pragma unroll
+    for (int t = 0; t < U; ++t) {
+      const int64_t row = base + t * RPL + sub;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (b >= B) break;
+        const float s = group_sum<LPR>(dot8_bf16(cur[t], zc[b], 0.f));
+        if (c == 0 && row < whi) sc[b][row - blo] = s;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < U; ++t) cur[t] = nxt[t];
+  }
+  __syncthreads();
+  if (wave < B) {
+    const int b = wave;
+    const int nrows = (int)(bhi - blo);
+    uint64_t key[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = e * kWave + lane;
+      key[e] = j < nrows ? cand_key(sc[b][j], (int)(blo + j)) : 0ull;
+    }
+    const uint64_t T = wave_select_threshold<E>(key, k);
+    const int64_t o = ((int64_t)b * nblk + blockIdx.x) * k;
+    wave_emit_sorted<E>(key, T, k, tmp[b], part_s + o, part_i + o);
+  }
+}
+
+// -------------------------------------------- score pass, long rows (W . h)
+// One vocabulary row at a time per wave: NL wave loads of 1 KiB (K <= NL *
+// 512), the next row's loads issued before the current row is reduced. The
+// rows of H sit in LDS. Loads past K read a clamped address and are zeroed.
+template <int NB, int NL>
+__global__ void __launch_bounds__(kSmallThreads) select_long_kernel(
+    const uint16_t* __restrict__ M, const uint16_t* __restrict__ X, int64_t V, int K, int B, int k,
+    float* __restrict__ part_s, int* __restrict__ part_i) {
+  __shared__ SmallLds<NB> sm;
+  __shared__ u32x4 xs[NB][NL * kWave];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int e = threadIdx.x; e < NB * NL * kWave; e += kSmallThreads) {
+    const int b = e / (NL * kWave), rem = e - b * NL * kWave;
+    const int col = rem * 8;
+    xs[b][rem] = (b < B && col < K) ? load16(X + (int64_t)b * K + col) : u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+
+  const int64_t nblk = gridDim.x;
+  const int64_t blo = V * blockIdx.x / nblk, bhi = V * (blockIdx.x + 1) / nblk;
+  const int64_t wlo = blo + (bhi - blo) * wave / kWavesSmall;
+  const int64_t whi = blo + (bhi - blo) * (wave + 1) / kWavesSmall;
+  const int64_t last = whi - 1;
+
+  WaveSel<NB> st;
+  st.init();
+  u32x4 cur[NL], nxt[NL];
+  int cols[NL];
+#pragma unroll
+  for (int t = 0; t < NL; ++t) {
+    const int col = (t * kWave + lane) * 8;
+    cols[t] = col < K ? col : K - 8;
+  }
+  if (wlo < whi) {
+#pragma unroll
+    for (int t = 0; t < NL; ++t) cur[t] = load16(M + wlo * K + cols[t]);
+  }
+  for (int64_t row = wlo; row < whi; ++row) {
+    const int64_t nr = row + 1 < last ? row + 1 : last;
+#pragma unroll
+    for (int t = 0; t < NL; ++t) nxt[t] = load16(M + nr * K + cols[t]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b >= B) break;
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < NL; ++t) acc = dot8_bf16(cur[t], xs[b][t * kWave + lane], acc);
+      const float s = group_sum<kWave>(acc);
+      const bool pass = lane == 0 && precedes(s, (int)row, st.ts[b], st.ti[b]);
+      st.push(b, pass, s, (int)row, sm.bs[wave][b], sm.bi[wave][b]);
+      if (st.cnt[b] >= kBuf) st.fold(b, sm.bs[wave][b], sm.bi[wave][b], k);
+    }
+#pragma unroll
+    for (int t = 0; t < NL; ++t) cur[t] = nxt[t];
+  }
+  finish_block<NB>(sm, st, B, k, part_s, part_i);
+}
+
+// ================================================================ launchers
+
+constexpr int kMaxSmallBlocks = 512;
+
+int small_blocks(int64_t V) {
+  int64_t n = (V + 255) / 256;   // >= 64 rows per wave
+  if (n > kMaxSmallBlocks) n = kMaxSmallBlocks;
+  return (int)(n < 1 ? 1 : n);
+}
+
+bool small_path(int dtype, int64_t B, int64_t K_lowrank, int64_t V) {
+  if (dtype != 0 || B > kSmallB) return false;
+  if (V > (int64_t)kMaxSmallBlocks * kBlockRows) return false;   // rows per block
+  return K_lowrank >= 8 && K_lowrank <= 512 && (K_lowrank & (K_lowrank - 1)) == 0;
+}
+
+constexpr int kMaxRowLoads = 16;   // rows up to 8192 elements
+
+bool small_long_path(int dtype, int64_t B, int64_t K, int64_t V) {
+  return dtype == 0 && B <= kSmallB && K <= kMaxRowLoads * kWave * 8 &&
+         V <= (int64_t)kMaxSmallBlocks * kBlockRows;
+}
+
+// Wave loads (of 512 elements) per row, rounded up to an instantiated count.
+static int row_loads(int K) {
+  const int nl = (K + kWave * 8 - 1) / (kWave * 8);
+  static const int kCounts[] = {1, 2, 4, 6, 8, 10, 12, 16};
+  for (int c : kCounts)
+    if (nl <= c) return c;
+  return -1;
+}
+
+#define LRH_NL_DISPATCH(nl, body)       \
+  do {                                  \
+    switch (nl) {                       \
+      case 1: { constexpr int NL = 1; body; } break;   \
+      case 2: { constexpr int NL = 2; body; } break;   \
+      case 4: { constexpr int NL = 4; body; } break;   \
+      case 6: { constexpr int NL = 6; body; } break;   \
+      case 8: { constexpr int NL = 8; body; } break;   \
+      case 10: { constexpr int NL = 10; body; } break; \
+      case 12: { constexpr int NL = 12; body; } break; \
+      case 16: { constexpr int NL = 16; body; } break; \
+      default: return hipErrorInvalidValue;            \
+    }                                   \
+  } while (0)
+
+#define LRH_NB_DISPATCH(B, body) \
+  do {                           \
+    if ((B) <= 1) {              \
+      constexpr int NB = 1;      \
+      body;                      \
+    } else if ((B) == 2) {       \
+      constexpr int NB = 2;      \
+      body;                      \
+    } else {                     \
+      constexpr int NB = 4;      \
+      body;                      \
+    }                            \
+  } while (0)
+
+hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream) {
+  dim3 grid((r + kWavesSmall - 1) / kWavesSmall);
+  const int nl = row_loads(d);
+  if (nl < 0) return launch_down(0, Q, H, r, d, B, Z, stream);   // rows longer than 8192
+  LRH_NB_DISPATCH(B, LRH_NL_DISPATCH(nl, hipLaunchKernelGGL((down_small_kernel<NB, NL>), grid,
+                                                               dim3(kSmallThreads), 0, stream, (const uint16_t*)Q,
+                                                               (const uint16_t*)H, r, d, (int)B, (uint16_t*)Z)));
+  return hipGetLastError();
+}
+
+template <int K>
+static hipError_t launch_short_k(const void* M, const void* X, int64_t V, int64_t B, int k, float* ps, int* pi,
+                                 hipStream_t stream) {
+  const int nblk = small_blocks(V);
+  dim3 grid(nblk);
+  const int64_t rows = (V + nblk - 1) / nblk;   // most rows of one block
+  if (rows <= 4 * kWave) {
+    LRH_NB_DISPATCH(B, hipLaunchKernelGGL((select_short_kernel<K, NB, 4>), grid, dim3(kSmallThreads), 0, stream,
+                                          (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
+  } else if (rows <= 5 * kWave) {
+    LRH_NB_DISPATCH(B, hipLaunchKernelGGL((select_short_kernel<K, NB, 5>), grid, dim3(kSmallThreads), 0, stream,
+                                          (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
+  } else {
+    LRH_NB_DISPATCH(B, hipLaunchKernelGGL((select_short_kernel<K, NB, 8>), grid, dim3(kSmallThreads), 0, stream,
+                                          (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* ps,
+                               int* pi, hipStream_t stream) {
+  switch (K) {
+    case 8: return launch_short_k<8>(M, X, V, B, k, ps, pi, stream);
+    case 16: return launch_short_k<16>(M, X, V, B, k, ps, pi, stream);
+    case 32: return launch_short_k<32>(M, X, V, B, k, ps, pi, stream);
+    case 64: return launch_short_k<64>(M, X, V, B, k, ps, pi, stream);
+    case 128: return launch_short_k<128>(M, X, V, B, k, ps, pi, stream);
+    case 256: return launch_short_k<256>(M, X, V, B, k, ps, pi, stream);
+    case 512: return launch_short_k<512>(M, X, V, B, k, ps, pi, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* ps,
+                              int* pi, hipStream_t stream) {
+  dim3 grid(small_blocks(V));
+  const int nl = row_loads(K);
+  LRH_NB_DISPATCH(B, LRH_NL_DISPATCH(nl, hipLaunchKernelGGL((select_long_kernel<NB, NL>), grid,
+                                                               dim3(kSmallThreads), 0, stream, (const uint16_t*)M,
+                                                               (const uint16_t*)X, V, K, (int)B, k, ps, pi)));
+  return hipGetLastError();
+}
+
+}  // namespace lrh

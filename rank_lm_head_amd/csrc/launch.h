@@ -7,8 +7,29 @@
 
 namespace lrh {
 
-// Vocabulary slices of the selection pass for B rows over V tokens. The
-// same plan sizes the workspace, so it must depend only on (B, V).
+// Draft-row counts up to this use the streaming (vector ALU) kernels of
+// kernels_small.hip; larger batches use the matrix-core kernels.
+constexpr int kSmallB = 4;
+
+// ----------------------------------------------------- kernels_small.hip
+// Blocks (= candidate lists per row) of the streaming selection over V rows.
+int small_blocks(int64_t V);
+// Whether a call with B rows and rank (row length) K takes the streaming path.
+bool small_path(int dtype, int64_t B, int64_t K, int64_t V);
+bool small_long_path(int dtype, int64_t B, int64_t K, int64_t V);
+
+// z = round(Q . h) for B <= 4 rows.
+hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream);
+// Streaming score pass: per block, the k best of its slice for each row,
+// written to part_[row][block][0..k).
+hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
+                               int* part_i, hipStream_t stream);
+hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
+                              int* part_i, hipStream_t stream);
+
+// ------------------------------------------------------ kernels_mfma.hip
+// Vocabulary slices of the matrix-core selection pass for B rows over V
+// tokens. The same plan sizes the workspace, so it depends only on (B, V).
 int plan_vsplit(int64_t B, int64_t V);
 
 // z = round(Q . h) for B rows: Z is B x r in the weight dtype.
@@ -20,16 +41,20 @@ hipError_t launch_down(int dtype, const void* Q, const void* H, int r, int d, in
 hipError_t launch_select(int dtype, const void* M, const void* X, int64_t V, int K, int64_t B,
                          int k, int n_vsplit, float* part_s, int* part_i, hipStream_t stream);
 
-// Merges n_parts sorted lists of k per row into idx / score (score may be NULL).
-hipError_t launch_merge(const float* part_s, const int* part_i, int n_parts, int64_t B, int k,
-                        int32_t* idx, float* score, hipStream_t stream);
+// Dense logits[b, v] = W[v, :] . h_b for all V (test aid).
+hipError_t launch_dense(int dtype, const void* W, const void* H, int64_t V, int d, int64_t B,
+                        float* logits, hipStream_t stream);
+
+// ----------------------------------------------------- kernels_merge.hip
+// Merges n sorted lists of k per row (part_[row][list][k], n <= 512) into
+// idx / score (score may be NULL). With logits != NULL, also writes the
+// winners' exact logits W[id] . h_b.
+hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int64_t V, int64_t B, int k,
+                        const void* W, const void* H, int d, int32_t* idx, float* score, float* logits,
+                        hipStream_t stream);
 
 // logits[b, j] = W[idx[b, j], :] . h_b (NaN for ids outside [0, V)).
 hipError_t launch_rescore(int dtype, const void* W, const void* H, const int32_t* idx, int64_t B,
                           int k, int64_t V, int d, float* logits, hipStream_t stream);
-
-// Dense logits[b, v] = W[v, :] . h_b for all V (test aid).
-hipError_t launch_dense(int dtype, const void* W, const void* H, int64_t V, int d, int64_t B,
-                        float* logits, hipStream_t stream);
 
 }  // namespace lrh

@@ -28,6 +28,8 @@ struct lrhead_s {
   void* z;          // B_max x r, weight dtype
   float* part_s;    // candidate lists: rows x slices x k_max
   int* part_i;
+  hipEvent_t ev_before;  // optional events around the selection kernel
+  hipEvent_t ev_after;
 };
 
 namespace {
@@ -57,11 +59,16 @@ struct Layout {
   size_t z, part_s, part_i, total;
 };
 
-// Most candidate-list rows any call with B <= B_max writes (B x slices).
+// Most candidate lists any call with B <= B_max writes (B x slices), over
+// both the streaming and the matrix-core selection.
 int64_t max_list_rows(int64_t B_max, int64_t V) {
   int64_t best = 0;
   for (int64_t B = 1; B <= B_max; ++B) {
-    const int64_t rows = B * lrh::plan_vsplit(B, V);
+    int64_t rows = B * lrh::plan_vsplit(B, V);
+    if (B <= lrh::kSmallB) {
+      const int64_t small = B * lrh::small_blocks(V);
+      if (small > rows) rows = small;
+    }
     if (rows > best) best = rows;
   }
   return best;
@@ -124,13 +131,35 @@ int check_out(const void* p, const char* name, bool required) {
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
 
-int enqueue_candidates(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, float* score,
-                       hipStream_t s) {
-  LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
-  const int nvs = lrh::plan_vsplit(B, h->V);
-  LRH_HIP(lrh::launch_select(h->dtype, h->P, h->z, h->V, (int)h->r, B, k, nvs, h->part_s, h->part_i, s),
-          "score/selection launch");
-  LRH_HIP(lrh::launch_merge(h->part_s, h->part_i, nvs, B, k, idx, score, s), "merge launch");
+int record(hipEvent_t ev, hipStream_t s) {
+  if (!ev) return LRHEAD_OK;
+  const hipError_t e = hipEventRecord(ev, s);
+  return e == hipSuccess ? LRHEAD_OK : hip_fail(e, "hipEventRecord");
+}
+
+// Down-projection, score pass with per-slice selection, and the merge of
+// the slice lists; with `logits`, the merge also rescores the winners.
+int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, float* score, float* logits,
+                 hipStream_t s) {
+  int n_lists;
+  if (lrh::small_path(h->dtype, B, h->r, h->V)) {
+    LRH_HIP(lrh::launch_down_small(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
+    LRH_TRY(record(h->ev_before, s));
+    LRH_HIP(lrh::launch_select_small(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, s),
+            "score/selection launch");
+    LRH_TRY(record(h->ev_after, s));
+    n_lists = lrh::small_blocks(h->V);
+  } else {
+    LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
+    n_lists = lrh::plan_vsplit(B, h->V);
+    LRH_TRY(record(h->ev_before, s));
+    LRH_HIP(lrh::launch_select(h->dtype, h->P, h->z, h->V, (int)h->r, B, k, n_lists, h->part_s, h->part_i, s),
+            "score/selection launch");
+    LRH_TRY(record(h->ev_after, s));
+  }
+  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, h->V, B, k, h->W, H, (int)h->d, idx, score,
+                            logits, s),
+          "merge launch");
   return LRHEAD_OK;
 }
 
@@ -180,6 +209,8 @@ int lrhead_create(lrhead_t* out, int dtype, int64_t V, int64_t d, int64_t r, con
   h->z = h->ws + L.z;
   h->part_s = reinterpret_cast<float*>(h->ws + L.part_s);
   h->part_i = reinterpret_cast<int*>(h->ws + L.part_i);
+  h->ev_before = nullptr;
+  h->ev_after = nullptr;
   *out = h;
   return LRHEAD_OK;
 }
@@ -191,7 +222,7 @@ int lrhead_candidates(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx,
   LRH_TRY(check_out(idx, "idx", B > 0));
   LRH_TRY(check_out(score, "score", false));
   if (B == 0) return LRHEAD_OK;
-  return enqueue_candidates(h, H, B, k, idx, score, static_cast<hipStream_t>(stream));
+  return enqueue_head(h, H, B, k, idx, score, nullptr, static_cast<hipStream_t>(stream));
 }
 
 int fullhead_logits(lrhead_t h, const void* H, int64_t B, const int32_t* idx, int k, float* logits,
@@ -219,10 +250,23 @@ int fullhead_topk(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, flo
   LRH_TRY(check_out(logits, "logits", B > 0));
   if (B == 0) return LRHEAD_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int nvs = lrh::plan_vsplit(B, h->V);
-  LRH_HIP(lrh::launch_select(h->dtype, h->W, H, h->V, (int)h->d, B, k, nvs, h->part_s, h->part_i, s),
-          "full-head selection launch");
-  LRH_HIP(lrh::launch_merge(h->part_s, h->part_i, nvs, B, k, idx, logits, s), "merge launch");
+  int n_lists;
+  if (lrh::small_long_path(h->dtype, B, h->d, h->V)) {
+    n_lists = lrh::small_blocks(h->V);
+    LRH_TRY(record(h->ev_before, s));
+    LRH_HIP(lrh::launch_select_long(h->W, H, h->V, (int)h->d, B, k, h->part_s, h->part_i, s),
+            "full-head selection launch");
+    LRH_TRY(record(h->ev_after, s));
+  } else {
+    n_lists = lrh::plan_vsplit(B, h->V);
+    LRH_TRY(record(h->ev_before, s));
+    LRH_HIP(lrh::launch_select(h->dtype, h->W, H, h->V, (int)h->d, B, k, n_lists, h->part_s, h->part_i, s),
+            "full-head selection launch");
+    LRH_TRY(record(h->ev_after, s));
+  }
+  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, h->V, B, k, nullptr, nullptr, (int)h->d, idx,
+                            logits, nullptr, s),
+          "merge launch");
   return LRHEAD_OK;
 }
 
@@ -235,9 +279,15 @@ int lrhead_draft(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, floa
   LRH_TRY(check_out(score, "score", false));
   LRH_TRY(check_out(logits, "logits", B > 0));
   if (B == 0) return LRHEAD_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  LRH_TRY(enqueue_candidates(h, H, B, k, idx, score, s));
-  LRH_HIP(lrh::launch_rescore(h->dtype, h->W, H, idx, B, k, h->V, (int)h->d, logits, s), "rescore launch");
+  return enqueue_head(h, H, B, k, idx, score, logits, static_cast<hipStream_t>(stream));
+}
+
+int lrhead_set_stage_events(lrhead_t h, void* before, void* after) {
+  LRH_TRY(check_handle(h));
+  if ((before == nullptr) != (after == nullptr))
+    return fail(LRHEAD_EINVAL, "give both events or neither");
+  h->ev_before = static_cast<hipEvent_t>(before);
+  h->ev_after = static_cast<hipEvent_t>(after);
   return LRHEAD_OK;
 }
 

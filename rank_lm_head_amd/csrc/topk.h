@@ -1,0 +1,278 @@
+// topk.h — candidate selection building blocks for the head's kernels.
+//
+// Order: (s1, i1) precedes (s2, i2) when s1 > s2, or s1 == s2 and i1 < i2
+// (the k best tokens, ties to the lower id). Pieces:
+//
+//  * WaveSel: a wave's running best-k for up to NB draft rows, when the
+//    wave's threshold is the same for all its lanes (a wave that owns whole
+//    vocabulary rows). The list is kept sorted in registers (one pair per
+//    lane), the k-th best in scalars, and rows that beat it are compacted
+//    into an LDS buffer with a ballot; a full buffer is folded into the list
+//    with a bitonic sort and a bitonic merge.
+//
+//  * wave_select_threshold / wave_emit_sorted: the exact k best of up to a
+//    few hundred keys held by one wave, by ballot-counted bisection (no
+//    sorting network on the hot path).
+//
+//  * merge_lists_seq: a wave-wide fold of sorted lists, the fallback of the
+//    merge kernel when too many entries tie at its threshold.
+#pragma once
+
+#include "device.h"
+
+namespace lrh {
+
+constexpr int kBuf = 64;            // per-row candidate buffer of a WaveSel
+
+// ------------------------------------------------------------------ WaveSel
+template <int NB>
+struct WaveSel {
+  float ls[NB];   // this lane's element of the sorted list
+  int li[NB];
+  float ts[NB];   // k-th best so far (wave-uniform)
+  int ti[NB];
+  int cnt[NB];    // buffered candidates (wave-uniform)
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      ls[b] = neg_inf();
+      li[b] = kSentinelId;
+      ts[b] = neg_inf();
+      ti[b] = kSentinelId;
+      cnt[b] = 0;
+    }
+  }
+
+  // Appends (s, v) of the lanes with `pass` to row b's buffer.
+  __device__ __forceinline__ void push(int b, bool pass, float s, int v, float* bs, int* bi) {
+    const unsigned long long m = __ballot(pass);
+    if (m) {
+      if (pass) {
+        const int p = cnt[b] + lanes_below(m);
+        bs[p] = s;
+        bi[p] = v;
+      }
+      cnt[b] += __popcll(m);
+    }
+  }
+
+  // Folds row b's buffer into its list and refreshes the k-th best.
+  __device__ __forceinline__ void fold(int b, const float* bs, const int* bi, int k) {
+    const int lane = threadIdx.x & 63;
+    float s = neg_inf();
+    int i = kSentinelId;
+    if (lane < cnt[b]) {
+      s = bs[lane];
+      i = bi[lane];
+    }
+    bitonic_sort_desc(s, i);
+    merge_reversed(s, i, __shfl(ls[b], kWave - 1 - lane), __shfl(li[b], kWave - 1 - lane));
+    ls[b] = s;
+    li[b] = i;
+    ts[b] = readlane_f(s, k - 1);
+    ti[b] = __builtin_amdgcn_readlane(i, k - 1);
+    cnt[b] = 0;
+  }
+};
+
+// ------------------------------------------------------- keys and counting
+// A candidate as one 64-bit key: the order-preserving image of its score in
+// the high word, the complement of its id in the low word. A larger key
+// precedes a smaller one, exactly the candidate order; 0 marks an empty slot
+// (every real key has a high word of at least 0x007FFFFF).
+__device__ __forceinline__ uint32_t order_key(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t cand_key(float s, int id) {
+  s = s + 0.0f;   // -0 and +0 are the same score
+  return ((uint64_t)order_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ uint32_t order_key_inv(uint32_t u) {
+  return (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+}
+__device__ __forceinline__ float key_score(uint64_t key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+__device__ __forceinline__ int key_id(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+
+__device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
+
+// Wave-wide min / max of a 32-bit value.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, (uint32_t)lane_xor<1>((int)x));
+  x = min(x, (uint32_t)lane_xor<2>((int)x));
+  x = min(x, (uint32_t)lane_xor<4>((int)x));
+  x = min(x, (uint32_t)lane_xor<8>((int)x));
+  x = min(x, (uint32_t)lane_xor<16>((int)x));
+  x = min(x, (uint32_t)lane_xor<32>((int)x));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)lane_xor<1>((int)x));
+  x = max(x, (uint32_t)lane_xor<2>((int)x));
+  x = max(x, (uint32_t)lane_xor<4>((int)x));
+  x = max(x, (uint32_t)lane_xor<8>((int)x));
+  x = max(x, (uint32_t)lane_xor<16>((int)x));
+  x = max(x, (uint32_t)lane_xor<32>((int)x));
+  return x;
+}
+
+// Wave-wide exact selection threshold over E keys per lane: returns T such
+// that exactly min(k, #non-empty keys) keys satisfy key >= T.
+//  1. Bisection on the score values inside [min, max] of the wave, counting
+//     with ballots and stopping as soon as exactly k scores reach the bound.
+//     The bound then separates the k-th and (k+1)-th scores, so a handful of
+//     halvings of the value range usually suffice.
+//  2. If the interval closes first (equal or adjacent scores at the
+//     boundary), an exact search on the keys: their high words (score
+//     images), then, among keys tied there, their low words (ids).
+template <int E>
+__device__ __forceinline__ uint64_t wave_select_threshold(const uint64_t (&key)[E], int k) {
+  int valid = 0;
+  float fmn = __builtin_inff(), fmx = -__builtin_inff();
+  float sv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    valid += wave_count(key[e] != 0);
+    sv[e] = key[e] != 0 ? key_score(key[e]) : -__builtin_inff();
+    if (key[e] != 0) {
+      fmn = fminf(fmn, sv[e]);
+      fmx = fmaxf(fmx, sv[e]);
+    }
+  }
+  if (valid <= k) return 1;
+  fmn = __uint_as_float(order_key_inv(wave_min_u32(order_key(fmn))));
+  fmx = __uint_as_float(order_key_inv(wave_max_u32(order_key(fmx))));
+  // count(s >= flo) >= k > count(s >= fhi); flo = min reaches all valid
+  float flo = fmn, fhi = fmx;
+  int cnt_hi = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) cnt_hi += wave_count(sv[e] >= fhi);
+  if (cnt_hi == k) return (uint64_t)order_key(fhi) << 32;
+  if (cnt_hi < k) {
+#pragma unroll 1
+    for (int it = 0; it < 64; ++it) {
+      const float mid = 0.5f * (flo + fhi);
+      if (!(mid > flo && mid < fhi)) break;   // adjacent floats
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) cnt += wave_count(sv[e] >= mid);
+      if (cnt == k) return (uint64_t)order_key(mid) << 32;
+      if (cnt > k)
+        flo = mid;
+      else
+        fhi = mid;
+    }
+  }
+  // exact search on the keys inside the bracket found so far:
+  // count(key high word >= lo) >= k > count(high word >= hi)
+  uint32_t kh[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) kh[e] = (uint32_t)(key[e] >> 32);
+  uint32_t lo = order_key(flo);
+  const uint64_t hi0 = cnt_hi < k ? (uint64_t)order_key(fhi) : (uint64_t)order_key(fmx) + 1;
+  uint64_t hi = hi0;
+#pragma unroll 1
+  while (hi - lo > 1) {
+    const uint32_t mid = (uint32_t)(lo + (hi - lo) / 2);
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cnt += wave_count(key[e] != 0 && kh[e] >= mid);
+    if (cnt >= k) {
+      lo = mid;
+      if (cnt == k) return (uint64_t)lo << 32;
+    } else {
+      hi = mid;
+    }
+  }
+  // lo is the k-th largest high word and several keys share it
+  int above = 0;
+  uint32_t lmn = 0xFFFFFFFFu, lmx = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    above += wave_count(key[e] != 0 && kh[e] > lo);
+    if (key[e] != 0 && kh[e] == lo) {
+      lmn = min(lmn, (uint32_t)key[e]);
+      lmx = max(lmx, (uint32_t)key[e]);
+    }
+  }
+  const int need = k - above;
+  uint32_t llo = wave_min_u32(lmn);
+  uint64_t lhi = (uint64_t)wave_max_u32(lmx) + 1;
+#pragma unroll 1
+  while (lhi - llo > 1) {
+    const uint32_t mid = (uint32_t)(llo + (lhi - llo) / 2);
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cnt += wave_count(key[e] != 0 && kh[e] == lo && (uint32_t)key[e] >= mid);
+    if (cnt >= need) {
+      llo = mid;
+      if (cnt == need) break;
+    } else {
+      lhi = mid;
+    }
+  }
+  return ((uint64_t)lo << 32) | llo;
+}
+
+// Writes the keys >= T (at most 64 of them) in candidate order to
+// out_s/out_i[0 .. n) and empty entries up to k; `tmp` is 64 words of LDS
+// owned by the wave. Returns n.
+template <int E>
+__device__ __forceinline__ int wave_emit_sorted(const uint64_t (&key)[E], uint64_t T, int k, uint64_t* tmp,
+                                                float* __restrict__ out_s, int* __restrict__ out_i) {
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool sel = key[e] != 0 && key[e] >= T;
+    const unsigned long long m = __ballot(sel);
+    if (sel) {
+      const int p = n + lanes_below(m);
+      if (p < kWave) tmp[p] = key[e];
+    }
+    n += __popcll(m);
+  }
+  if (n > kWave) n = kWave;
+  if (lane < n) {
+    const uint64_t mine = tmp[lane];
+    int r = 0;
+    for (int t = 0; t < n; ++t) r += tmp[t] > mine ? 1 : 0;
+    out_s[r] = key_score(mine);
+    out_i[r] = key_id(mine);
+  } else if (lane < k) {
+    out_s[lane] = neg_inf();
+    out_i[lane] = kSentinelId;
+  }
+  return n;
+}
+
+// ------------------------------------------------------- sequential merge
+// Wave-wide fallback: folds every list into (s, i), the running best 64 in
+// candidate order, skipping lists whose best entry does not beat the running
+// k-th.
+__device__ __forceinline__ void merge_lists_seq(const float* ps, const int* pi, int n, int k, float& s, int& i) {
+  const int lane = threadIdx.x & 63;
+  s = neg_inf();
+  i = kSentinelId;
+  const int j = kWave - 1 - lane;
+  for (int p = 0; p < n; ++p) {
+    const float head = ps[(int64_t)p * k];
+    const int head_i = pi[(int64_t)p * k];
+    const float ks = readlane_f(s, k - 1);
+    const int ki = __builtin_amdgcn_readlane(i, k - 1);
+    if (!precedes(head, head_i, ks, ki)) continue;
+    float os = neg_inf();
+    int oi = kSentinelId;
+    if (j < k) {
+      os = ps[(int64_t)p * k + j];
+      oi = pi[(int64_t)p * k + j];
+    }
+    merge_reversed(s, i, os, oi);
+  }
+}
+
+}  // namespace lrh

@@ -108,11 +108,14 @@ class Head:
                    "fullhead_logits(dense)")
         return out
 
-    def full_topk(self, H: torch.Tensor, k: int):
+    def full_topk(self, H: torch.Tensor, k: int, *, out=None):
         """Full-head baseline: (idx int32 [B, k], logits fp32 [B, k])."""
         B = self._rows(H)
-        idx = self._out((B, k), torch.int32)
-        logits = self._out((B, k), torch.float32)
+        if out is None:
+            idx = self._out((B, k), torch.int32)
+            logits = self._out((B, k), torch.float32)
+        else:
+            idx, logits = out
         _lib.check(self.lib.fullhead_topk(self._h, _ptr(H), B, k, _ptr(idx), _ptr(logits), self._stream()),
                    "fullhead_topk")
         return idx, logits
@@ -129,6 +132,10 @@ class Head:
         _lib.check(self.lib.lrhead_draft(self._h, _ptr(H), B, k, _ptr(idx), _ptr(score), _ptr(logits),
                                          self._stream()), "lrhead_draft")
         return idx, score, logits
+
+    def set_stage_events(self, before, after) -> None:
+        """Record two hipEvent_t handles (ints or None) around the selection kernel."""
+        _lib.check(self.lib.lrhead_set_stage_events(self._h, before, after), "lrhead_set_stage_events")
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:

@@ -95,6 +95,46 @@ def test_small_heads(dt, V, d, r, B, k):
     say(f"[ok] {stats}")
 
 
+@pytest.mark.parametrize("V,d,r,B,k", [
+    (5000, 256, 128, 3, 64),     # streaming path, 3 rows, k = 64
+    (30000, 512, 256, 4, 40),    # streaming path, 4 rows, many blocks
+    (777, 64, 32, 1, 5),
+    (300, 1032, 8, 2, 3),        # k < 4, r = 8, d not a multiple of 512
+    (9000, 8200, 64, 1, 16),     # d beyond the long-row kernel: matrix-core full head
+])
+def test_streaming_path_shapes(V, d, r, B, k):
+    inp = gen.make_custom(V, d, r, B, "bf16", seed=V + r)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=k)
+    say(f"[run] streaming V={V} d={d} r={r} B={B} k={k}")
+    idx, score, lg = head.draft(t["H"], k)
+    fidx, flog = head.full_topk(t["H"], k)
+    torch.cuda.synchronize()
+    errs, stats = check_lowrank(inp, k, np_(idx), np_(score), np_(lg))
+    assert not errs, errs[:5]
+    errs, _ = check_full(inp, k, np_(fidx), np_(flog))
+    assert not errs, errs[:5]
+    say(f"[ok] {stats}")
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_all_scores_tied(B):
+    """Every score equal: the k lowest ids win, in order (forces the merge's
+    exhaustive path, since every entry reaches the sampled threshold)."""
+    V, d, r, k = 5000, 128, 64, 32
+    inp = gen.make_custom(V, d, r, B, "bf16", seed=9)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    t["P"].zero_()
+    t["W"].zero_()
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=k)
+    idx, score, lg = head.draft(t["H"], k)
+    fidx, flog = head.full_topk(t["H"], k)
+    torch.cuda.synchronize()
+    want = np.tile(np.arange(k), (B, 1))
+    assert np.array_equal(np_(idx), want) and np.array_equal(np_(fidx), want)
+    assert not np.any(np_(score)) and not np.any(np_(lg)) and not np.any(np_(flog))
+
+
 def test_empty_batch_is_a_noop():
     inp = gen.make_custom(300, 64, 16, 4, "bf16", seed=1)
     t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
