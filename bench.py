@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", type=int, default=BENCH_CONFIG,
                     help="workload id (the headline is the batch-1 bf16 drafter head)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB with a plain device copy, so "
+                         "that hardware byte counters can be scaled against a known size")
     return ap.parse_args()
 
 
@@ -89,15 +92,15 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel: str, workload: str, per_launch_units: float):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if
-    they were taken on the current kernel sources; else None."""
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes (read + written) per launch of `kernel` from the committed
+    rocprofv3 counter summary (FETCH_SIZE / WRITE_SIZE, scaled by a copy of
+    known size), if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
     try:
-        data = json.load(open(path))
-        rec = data[workload][kernel]
+        rec = json.load(open(path))[workload][kernel]
     except Exception:
         return None
     if rec.get("kernel_hash") != kernel_hash():
@@ -269,7 +272,9 @@ def main() -> int:
     # plus the B rows of z.
     sel_bytes = cfg.V * cfg.r * s + cfg.B * cfg.r * s
     sel_gbs = sel_bytes / sel_s / 1e9
-    traffic = traffic_from_profiles("select_kernel", f"c{cid}", 1)
+    small = cfg.dtype == "bf16" and cfg.B <= 4 and cfg.r in (8, 16, 32, 64, 128, 256, 512)
+    sel_kernel = "select_short_kernel" if small else "select_mfma_kernel"
+    traffic = traffic_from_profiles(sel_kernel, f"c{cid}")
     call_bytes = (cfg.r * cfg.d + cfg.V * cfg.r + cfg.B * cfg.d + U * cfg.d) * s + cfg.B * cfg.k * 12
     call_flops = 2.0 * cfg.B * (cfg.r * cfg.d + cfg.V * cfg.r + cfg.k * cfg.d)
     full_bytes = cfg.V * cfg.d * s + cfg.B * cfg.d * s
@@ -296,7 +301,7 @@ def main() -> int:
         "call_bytes": call_bytes,
         "call_flops": call_flops,
         "distinct_W_rows": U,
-        "roofline": {"bound": "hbm", "kernel": "select_kernel (score pass + fused top-k)",
+        "roofline": {"bound": "hbm", "kernel": f"{sel_kernel} (score pass + per-slice top-k)",
                      "achieved": sel_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": sel_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "us_per_launch": sel_s * 1e6, "bytes_per_launch": sel_bytes},
@@ -304,6 +309,15 @@ def main() -> int:
                       "select_us_per_launch": full_sel_s * 1e6,
                       "hbm_frac": full_bytes / (full_sel_s) / (HBM_PEAK_GBS * 1e9)},
     }
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
     for h in heads:
