@@ -7,13 +7,12 @@
 // candidates cheaply, then score them exactly": the retrieved candidates are
 // scored exactly by the original full-rank head).
 //
-// Merge. Only lists whose best entry (head) is among the k best heads can
-// hold an overall winner: an entry of any other list is preceded by its own
-// head, which is preceded by k heads. And the k-th best head T precedes or
-// equals the k-th best entry overall, so only entries that reach T matter.
-// Wave 0 finds T among the heads by bisection (topk.h), the block collects
-// the entries of the k active lists that reach T (about k of them), and
-// wave 0 selects and orders the k best of those the same way.
+// Merge. Take any bound T that at least k list heads (best entries) reach.
+// Then at least k entries reach T, so an entry below T is preceded by k
+// others and cannot win, and a list whose head is below T holds no winner.
+// Wave 0 finds a T that between k and 64 heads reach (windowed bisection,
+// topk.h), the block collects the entries of those active lists that reach
+// T (a few k of them), and wave 0 ranks the k best of those.
 //
 // Rescoring: logit = W[id, :] . h with fp32 accumulation, one wave per
 // candidate, every load of the W row and of h issued before the products.
@@ -117,7 +116,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
   const float* ps = part_s + b * n * k;
   const int* pi = part_i + b * n * k;
 
-  // 1. the k-th best head T (wave 0); the lists whose head reaches T
+  // 1. a bound T that between k and 64 heads reach (wave 0); the lists whose head reaches T
   if (wave == 0) {
     // all loads first, from clamped (valid) addresses, then the keys
     float hs[kHeadE];
@@ -132,7 +131,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
 #pragma unroll
     for (int e = 0; e < kHeadE; ++e)
       key[e] = (e * kWave + lane < n && hid[e] != kSentinelId) ? cand_key(hs[e], hid[e]) : 0ull;
-    const uint64_t T1 = wave_select_threshold<kHeadE>(key, k);
+    const uint64_t T1 = wave_window_threshold<kHeadE>(key, k, kWave);
     int na = 0;
 #pragma unroll
     for (int e = 0; e < kHeadE; ++e) {
@@ -190,8 +189,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
         const int j = e * kWave + lane;
         key[e] = j < nc ? m.cand[j] : 0ull;
       }
-      const uint64_t T2 = wave_select_threshold<kCandE>(key, k);
-      wave_emit_sorted<kCandE>(key, T2, k, m.tmp, m.top_s, m.top_i);
+      wave_topk_emit<kCandE>(key, k, m.tmp, m.top_s, m.top_i);
     } else {
       float s;
       int i;

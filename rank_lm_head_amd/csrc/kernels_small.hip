@@ -103,8 +103,8 @@ __device__ __forceinline__ void finish_block(SmallLds<NB>& sm, WaveSel<NB>& st, 
 // [V*x/n, V*(x+1)/n) (at most kBlockRows rows) and each wave a quarter of
 // it; the next U wave loads are issued before the current ones are used.
 // The scores go to LDS, and after the pass wave b finds the k best of the
-// slice for row b by bisection (topk.h) and writes them, in order, to
-// part_[b][x][0..k).
+// slice for row b (windowed bisection and counting ranks, topk.h) and writes
+// them, in order, to part_[b][x][0..k).
 constexpr int kBlockRows = 512;
 
 template <int K, int NB, int E>
@@ -170,9 +170,8 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
       const int j = e * kWave + lane;
       key[e] = j < nrows ? cand_key(sc[b][j], (int)(blo + j)) : 0ull;
     }
-    const uint64_t T = wave_select_threshold<E>(key, k);
     const int64_t o = ((int64_t)b * nblk + blockIdx.x) * k;
-    wave_emit_sorted<E>(key, T, k, tmp[b], part_s + o, part_i + o);
+    wave_topk_emit<E>(key, k, tmp[b], part_s + o, part_i + o);
   }
 }
 

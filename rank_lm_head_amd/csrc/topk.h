@@ -10,9 +10,14 @@
 //    into an LDS buffer with a ballot; a full buffer is folded into the list
 //    with a bitonic sort and a bitonic merge.
 //
-//  * wave_select_threshold / wave_emit_sorted: the exact k best of up to a
-//    few hundred keys held by one wave, by ballot-counted bisection (no
-//    sorting network on the hot path).
+//  * wave_window_threshold / wave_topk_emit: the k best of up to a few
+//    hundred keys held by one wave. A short bisection on the score values
+//    finds a bound that between k and 64 keys reach; those are compacted
+//    to LDS and each is placed by counting the keys that precede it, which
+//    orders them as well (no sorting network on the hot path).
+//
+//  * wave_select_threshold / wave_emit_sorted: the exact k-th best by a
+//    full bisection, used when ties keep the window from being reached.
 //
 //  * merge_lists_seq: a wave-wide fold of sorted lists, the fallback of the
 //    merge kernel when too many entries tie at its threshold.
@@ -248,6 +253,100 @@ __device__ __forceinline__ int wave_emit_sorted(const uint64_t (&key)[E], uint64
     out_i[lane] = kSentinelId;
   }
   return n;
+}
+
+// ------------------------------------------------ windowed selection
+// A bound T with k <= #{key >= T} <= cap (cap <= 64) over E keys per lane,
+// found by bisection on the score values: only the window has to be hit,
+// not the gap between the k-th and (k+1)-th score, so a few halvings of the
+// wave's value range suffice. Returns 1 (every non-empty key) when at most
+// cap keys are non-empty; falls back to the exact k-th key when ties at the
+// boundary keep the window out of reach.
+template <int E>
+__device__ __forceinline__ uint64_t wave_window_threshold(const uint64_t (&key)[E], int k, int cap) {
+  int valid = 0;
+  float fmn = __builtin_inff(), fmx = -__builtin_inff();
+  float sv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    valid += wave_count(key[e] != 0);
+    sv[e] = key[e] != 0 ? key_score(key[e]) : -__builtin_inff();
+    if (key[e] != 0) {
+      fmn = fminf(fmn, sv[e]);
+      fmx = fmaxf(fmx, sv[e]);
+    }
+  }
+  if (valid <= cap) return 1;
+  fmn = __uint_as_float(order_key_inv(wave_min_u32(order_key(fmn))));
+  fmx = __uint_as_float(order_key_inv(wave_max_u32(order_key(fmx))));
+  // invariant: count(s >= flo) > cap and count(s >= fhi) < k
+  float flo = fmn, fhi = fmx;
+  int c = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) c += wave_count(sv[e] >= fhi);
+  if (c >= k) {
+    if (c <= cap) return (uint64_t)order_key(fhi) << 32;
+  } else {
+#pragma unroll 1
+    for (int it = 0; it < 64; ++it) {
+      const float mid = 0.5f * (flo + fhi);
+      if (!(mid > flo && mid < fhi)) break;
+      c = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) c += wave_count(sv[e] >= mid);
+      if (c >= k && c <= cap) return (uint64_t)order_key(mid) << 32;
+      if (c > cap)
+        flo = mid;
+      else
+        fhi = mid;
+    }
+  }
+  return wave_select_threshold<E>(key, k);
+}
+
+// Places the n <= 64 distinct keys tmp[0 .. n) by counting, for each, the
+// keys that precede it; the k best go to out_s/out_i[0 .. k) in candidate
+// order and empty entries fill out[n .. k) when n < k.
+__device__ __forceinline__ void wave_rank_emit(const uint64_t* tmp, int n, int k, float* __restrict__ out_s,
+                                               int* __restrict__ out_i) {
+  const int lane = threadIdx.x & 63;
+  if (lane < n) {
+    const uint64_t mine = tmp[lane];
+    int r = 0;
+#pragma unroll 8
+    for (int t = 0; t < n; ++t) r += tmp[t] > mine ? 1 : 0;
+    if (r < k) {
+      out_s[r] = key_score(mine);
+      out_i[r] = key_id(mine);
+    }
+  } else if (lane < k) {
+    out_s[lane] = neg_inf();
+    out_i[lane] = kSentinelId;
+  }
+}
+
+// The k best of E keys per lane (distinct where non-empty), in candidate
+// order, to out_s/out_i[0 .. k); `tmp` is 64 words of LDS owned by the wave.
+template <int E>
+__device__ __forceinline__ void wave_topk_emit(const uint64_t (&key)[E], int k, uint64_t* tmp,
+                                               float* __restrict__ out_s, int* __restrict__ out_i) {
+  const uint64_t T = wave_window_threshold<E>(key, k, kWave);
+  int n = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool sel = key[e] != 0 && key[e] >= T;
+    const unsigned long long m = __ballot(sel);
+    if (sel) {
+      const int p = n + lanes_below(m);
+      if (p < kWave) tmp[p] = key[e];
+    }
+    n += __popcll(m);
+  }
+  n = min(n, kWave);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  wave_rank_emit(tmp, n, k, out_s, out_i);
 }
 
 // ------------------------------------------------------- sequential merge
