@@ -1,0 +1,566 @@
+// kernels_gemm.hip — the vocabulary pass on the matrix cores for row
+// batches (bf16, B > 4): S = X . M^T with M = P (low-rank scores, K = r) or
+// M = W (full-head logits, K = d), followed by an exact per-row top-k
+// ("EAGLE-4", section "Retrieve vocabulary candidates cheaply, then score
+// them exactly": the k best candidates of every draft row over the whole
+// vocabulary).
+//
+// S is B x V and never stored whole. The selection uses a per-row bound:
+//
+//   1. Sample pass. The same GEMM over every `stride`-th block of vocabulary
+//      rows keeps, per draft row, the maximum of each 16-row tile. The k-th
+//      largest of those maxima, theta_b, is reached by at least k distinct
+//      scores of row b (one per tile), so it is a lower bound of the row's
+//      k-th best score.
+//   2. Main pass. The GEMM over all vocabulary rows writes only the scores
+//      that reach theta_b (a few hundred per row), each at its own column of
+//      a sparse B x V score array, with a bit mask per 32 of them.
+//   3. Collect. One block per row gathers the flagged scores and ranks the k
+//      best (windowed bisection and counting ranks, topk.h); a row with more
+//      than a buffer's worth of flagged scores (heavy ties) is taken in
+//      rounds, so the result is exact in every case.
+//
+// Both passes compute every 16x16 tile with the same MFMA sequence (same
+// operands, same k order), so the bound of the sample pass holds bit for bit
+// in the main pass.
+//
+// GEMM layout: a block computes a BM x BN tile of S^T (BM vocabulary rows x
+// BN draft rows) with 4 waves in a WM x WN grid; K advances in stages of 64
+// bf16 copied from global memory straight into LDS (three stage buffers: two
+// stages in flight while the third feeds the matrix cores). In LDS each row
+// of a stage is 8 chunks of 16 bytes, chunk c of row r stored at position
+// c ^ (r & 7), so the 16-byte fragment reads of eight consecutive rows hit
+// distinct banks.
+// Blocks are numbered so that the BN-tiles of one vocabulary block run on the
+// same XCD (consecutive workgroup ids go to consecutive XCDs), which keeps
+// the shared M tile in that XCD's L2.
+#include "launch.h"
+#include "topk.h"
+
+namespace lrh {
+
+constexpr int kGemmThreads = 256;
+constexpr int kBK = 64;                  // K elements per LDS stage
+constexpr int kRowChunks = kBK / 8;      // 16-byte chunks per row per stage
+constexpr int kXcds = 8;
+constexpr int kStages = 3;               // LDS stage buffers
+constexpr int kMaxSampleTiles = 2048;    // tile maxima per row kept by the sample pass
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int TM = BM / WM, TN = BN / WN;   // wave tile
+  static constexpr int FM = TM / 16, FN = TN / 16;   // 16x16 tiles per wave
+  static constexpr int A_LD = BM * kRowChunks / kGemmThreads;
+  static constexpr int B_LD = BN * kRowChunks / kGemmThreads;
+  static_assert(WM * WN == 4, "four waves");
+  static_assert(FM * 4 <= 32, "a wave's rows of one column fit a 32-bit mask per lane group");
+  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the loaders");
+};
+
+enum { kModeMax = 0, kModeFilter = 1 };
+
+__device__ __forceinline__ int swz(int row, int c) { return row * kRowChunks + (c ^ (row & 7)); }
+
+// Operand rows [row0, row0 + rows) of a row-major bf16 matrix with K
+// columns, copied stage by stage (64 columns) from global memory straight
+// into LDS (buffer loads with the LDS as destination, 16 bytes per lane).
+// One such load of a wave fills 1 KiB of LDS, lane l the l-th 16 bytes,
+// i.e. 8 rows of the stage; lane l therefore fetches chunk
+// (l % 8) ^ (row & 7) of its row so that the swizzled layout comes out.
+// Rows past the matrix and columns past K get an offset beyond the
+// resource's size and read as zeros. Flags: raw (untyped) dword access.
+constexpr int kRawBufferFlags = 0x00020000;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// The wave's index in the block, as a value the compiler knows to be
+// uniform (it feeds the LDS destination register of the copies).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+
+template <int LD>
+struct StageDma {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[LD];   // byte offset of the lane's chunk in stage 0
+  int col[LD];        // first column of the lane's chunk in stage 0
+  uint32_t oob;       // an offset past the resource
+
+  __device__ __forceinline__ void init(const uint16_t* __restrict__ base, int64_t row0, int64_t nrows, int K) {
+    const int64_t valid = nrows - row0;   // >= 1
+    const uint32_t bytes = uniform_u32((uint32_t)(valid * K * 2));
+    const uint64_t addr = reinterpret_cast<uint64_t>(base + row0 * (int64_t)K);
+    const uint64_t ua = ((uint64_t)uniform_u32((uint32_t)(addr >> 32)) << 32) | uniform_u32((uint32_t)addr);
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ua), (short)0, (int)bytes, kRawBufferFlags);
+    oob = bytes;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      const int row = (i * 4 + wave) * 8 + lane / 8;
+      const int c = (lane % 8) ^ (row & 7);
+      col[i] = c * 8;
+      off[i] = row < valid ? (uint32_t)(row * K + c * 8) * 2u : oob;
+    }
+  }
+
+  // Wave w's loads of stage kc into `stage` (LDS, BM or BN rows x 128 B).
+  __device__ __forceinline__ void issue(u32x4* stage, int kc, int K, bool tail) const {
+    const int wave = wave_id();
+#pragma unroll
+    for (int i = 0; i < LD; ++i) {
+      const uint32_t o = (tail && kc * kBK + col[i] >= K) ? oob : off[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(stage + (i * 4 + wave) * kWave), 16, (int)o,
+                                               kc * kBK * 2, 0, 0);
+    }
+  }
+};
+
+// A block barrier that orders LDS accesses only: unlike __syncthreads it
+// does not wait for the stage copies still in flight (the explicit
+// wait_vmcnt before it decides which of those must have landed).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are done
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Waits until at most N of this wave's vector memory operations are
+// outstanding (s_waitcnt vmcnt(N), the other counters unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+__device__ __forceinline__ float fmax_lanes(float m) {
+  m = fmaxf(m, __int_as_float(lane_xor<16>(__float_as_int(m))));
+  m = fmaxf(m, __int_as_float(lane_xor<32>(__float_as_int(m))));
+  return m;
+}
+
+// Grid: 1-D, round_up(nvb, 8) * ceil(B / BN) blocks (see the XCD mapping
+// above); nvb vocabulary blocks of BM rows, the s-th being block s * stride.
+//  kModeMax:    aux_f = tile maxima, row n at aux_f + n * ns_tiles, tile
+//               index s * (BM/16) + (16-row tile within the block).
+//  kModeFilter: theta = per-row bound; S = sparse scores (row n at
+//               S + n * ldS); mask = per row NW words, word
+//               ((vb * WM + wm) * 4 + g) holds bit (i * 4 + q) for vocabulary
+//               row (vb * WM + wm) * TM + i * 16 + 4 * g + q.
+template <class C, int MODE>
+__global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
+    const uint16_t* __restrict__ M, const uint16_t* __restrict__ X, int64_t V, int K, int64_t B, int nvb,
+    int stride, float* __restrict__ aux_f, int ns_tiles, const float* __restrict__ theta, float* __restrict__ S,
+    int64_t ldS, uint32_t* __restrict__ mask, int NW) {
+  extern __shared__ u32x4 lds[];
+  constexpr int SA = C::BM * kRowChunks, SB = C::BN * kRowChunks;   // 16-byte chunks per stage
+  const int nbuf = min(kStages, (K + kBK - 1) / kBK);   // stage buffers (fewer for short K)
+  u32x4* As = lds;                  // [nbuf][SA]
+  u32x4* Bs = lds + nbuf * SA;      // [nbuf][SB]
+
+  const int NT = (int)((B + C::BN - 1) / C::BN);
+  const int L = blockIdx.x;
+  const int xcd = L % kXcds, j = L / kXcds;
+  const int vb_local = (j / NT) * kXcds + xcd;
+  const int nt = j % NT;
+  if (vb_local >= nvb) return;
+  const int vb = vb_local * stride;
+  const int64_t m0 = (int64_t)vb * C::BM;
+  const int64_t n0 = (int64_t)nt * C::BN;
+
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int g = lane >> 4, col = lane & 15;
+
+  f32x4 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < C::FN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = (K + kBK - 1) / kBK;
+  const bool ktail = (K % kBK) != 0;
+  StageDma<C::A_LD> la;
+  StageDma<C::B_LD> lb;
+  la.init(M, m0, V, K);
+  lb.init(X, n0, B, K);
+  // Stages kc live in buffer kc % 3; two are in flight while one is used.
+  la.issue(As, 0, K, ktail && nk == 1);
+  lb.issue(Bs, 0, K, ktail && nk == 1);
+  if (nk > 1) {
+    la.issue(As + SA, 1, K, ktail && nk == 2);
+    lb.issue(Bs + SB, 1, K, ktail && nk == 2);
+  }
+  for (int kc = 0; kc < nk; ++kc) {
+    // this wave's copies of stage kc are done once only stage kc+1's remain
+    if (kc + 1 < nk)
+      wait_vmcnt<C::A_LD + C::B_LD>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();     // every wave's copies of stage kc landed; stage kc-1 is no longer read
+    if (kc + 2 < nk) {
+      const int nb = (kc + 2) % nbuf;
+      la.issue(As + nb * SA, kc + 2, K, ktail && kc + 2 == nk - 1);
+      lb.issue(Bs + nb * SB, kc + 2, K, ktail && kc + 2 == nk - 1);
+    }
+    const u32x4* as = As + (kc % nbuf) * SA;
+    const u32x4* bs = Bs + (kc % nbuf) * SB;
+    // both k-steps' fragments are read first, so the second step's LDS
+    // latency hides under the first step's matrix work
+    constexpr int KS = kBK / 32;
+    u32x4 fa[KS][C::FM], fb[KS][C::FN];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = s * 4 + g;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) fa[s][i] = as[swz(wm * C::TM + i * 16 + col, c)];
+#pragma unroll
+      for (int jn = 0; jn < C::FN; ++jn) fb[s][jn] = bs[swz(wn * C::TN + jn * 16 + col, c)];
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < C::FN; ++jn)
+          acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fa[s][i]),
+                                                               __builtin_bit_cast(bf16x8, fb[s][jn]), acc[i][jn], 0,
+                                                               0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, KS * (C::FM + C::FN), 0);   // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, KS * C::FM * C::FN, 0);     // then the MFMAs
+  }
+
+  // --------------------------------------------------------------- epilogue
+  const int64_t vrow = m0 + wm * C::TM + 4 * g;   // + i * 16 + q
+  if constexpr (MODE == kModeMax) {
+#pragma unroll
+    for (int jn = 0; jn < C::FN; ++jn) {
+      const int64_t n = n0 + wn * C::TN + jn * 16 + col;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        float m = neg_inf();
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (vrow + i * 16 + q < V) m = fmaxf(m, acc[i][jn][q]);
+        m = fmax_lanes(m);
+        if (g == 0 && n < B) aux_f[n * ns_tiles + vb_local * (C::BM / 16) + wm * C::FM + i] = m;
+      }
+    }
+  } else {
+    // Flags first, without branches (theta is waited for once, before any
+    // store), then the rare stores of flagged scores.
+    const bool full = m0 + C::BM <= V;
+    float th[C::FN];
+#pragma unroll
+    for (int jn = 0; jn < C::FN; ++jn) {
+      const int64_t n = n0 + wn * C::TN + jn * 16 + col;
+      th[jn] = theta[n < B ? n : B - 1];
+    }
+    uint32_t bits[C::FN];
+#pragma unroll
+    for (int jn = 0; jn < C::FN; ++jn) {
+      uint32_t b = 0;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) b |= (acc[i][jn][q] >= th[jn] ? 1u : 0u) << (i * 4 + q);
+      bits[jn] = b;
+    }
+    if (!full) {
+      uint32_t valid = 0;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) valid |= (vrow + i * 16 + q < V ? 1u : 0u) << (i * 4 + q);
+#pragma unroll
+      for (int jn = 0; jn < C::FN; ++jn) bits[jn] &= valid;
+    }
+#pragma unroll
+    for (int jn = 0; jn < C::FN; ++jn) {
+      const int64_t n = n0 + wn * C::TN + jn * 16 + col;
+      if (n >= B) continue;
+      mask[n * NW + ((int64_t)vb * C::WM + wm) * 4 + g] = bits[jn];
+      if (bits[jn] == 0) continue;
+      // the lane's 4 consecutive rows of a tile go out as one 16-byte store
+      // when any of them is flagged (only flagged ones are read back)
+      float* srow = S + n * ldS + vrow;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+        if ((bits[jn] >> (i * 4)) & 15u) *reinterpret_cast<f32x4*>(srow + i * 16) = acc[i][jn];
+    }
+  }
+}
+
+// --------------------------------------------------------- per-row bound
+// theta[b] = the k-th largest tile maximum of row b (or a slightly lower
+// value that between k and `cap` maxima reach); -inf when fewer than k
+// tiles exist. One wave per row.
+constexpr int kThetaE = kMaxSampleTiles / kWave;
+
+__global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ tmax, int ns_tiles, int64_t B, int k,
+                                                     int cap, float* __restrict__ theta) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= B) return;
+  const float* t = tmax + row * ns_tiles;
+  uint64_t key[kThetaE];
+  float vmin = __builtin_inff();
+#pragma unroll
+  for (int e = 0; e < kThetaE; ++e) {
+    const int j = e * kWave + lane;
+    const float m = t[j < ns_tiles ? j : ns_tiles - 1];
+    const bool ok = j < ns_tiles && m > neg_inf();
+    key[e] = ok ? cand_key(m, j) : 0ull;
+    if (ok) vmin = fminf(vmin, m);
+  }
+  int valid = 0;
+#pragma unroll
+  for (int e = 0; e < kThetaE; ++e) valid += wave_count(key[e] != 0);
+  float th = neg_inf();
+  if (valid >= k) {
+    const uint64_t T = wave_window_threshold<kThetaE>(key, k, cap);
+    if (T == 1) {
+      th = __uint_as_float(order_key_inv(wave_min_u32(order_key(vmin))));
+    } else {
+      th = key_score(T);
+    }
+  }
+  if (lane == 0) theta[row] = th;
+}
+
+// ----------------------------------------------------------------- collect
+constexpr int kCollectCap = 4096;                       // flagged scores per round
+constexpr int kCollectE = kCollectCap / kGemmThreads;   // keys per lane per wave
+
+struct CollectSmem {
+  uint64_t buf[kCollectCap];
+  uint64_t tmp[4][kWave];
+  float ws[5][kWave];       // lists 0..3: the waves' best; 4: running best
+  int wi[5][kWave];
+  int wave_tot[4];
+  int total;
+};
+
+// Exclusive prefix over the block of per-thread counts; returns the
+// thread's offset and writes the total to `total`.
+__device__ __forceinline__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int incl = x;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) before += wave_tot[w];
+    all += wave_tot[w];
+  }
+  if (threadIdx.x == 0) *total = all;
+  __syncthreads();
+  return before + incl - x;
+}
+
+// One block per row: the k best flagged scores of the row, in candidate
+// order, to idx / score (sentinel ids when fewer than k are flagged).
+template <int TM>
+__global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* __restrict__ mask, int NW,
+                                                                const float* __restrict__ S, int64_t ldS, int64_t B,
+                                                                int k, int32_t* __restrict__ idx,
+                                                                float* __restrict__ score) {
+  __shared__ CollectSmem m;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = blockIdx.x;
+  const uint32_t* mw = mask + row * NW;
+  const float* sr = S + row * ldS;
+
+  int cnt = 0;
+  for (int w = threadIdx.x; w < NW; w += kGemmThreads) cnt += __popc(mw[w]);
+  const int off = block_exclusive_scan(cnt, m.wave_tot, &m.total);
+  const int C = m.total;
+  if (threadIdx.x < kWave) {
+    m.ws[4][threadIdx.x] = neg_inf();
+    m.wi[4][threadIdx.x] = kSentinelId;
+  }
+  for (int base = 0; base < C; base += kCollectCap) {
+    int pos = off;
+    for (int w = threadIdx.x; w < NW; w += kGemmThreads) {
+      uint32_t bits = mw[w];
+      const int64_t slice = w >> 2, gq = w & 3;
+      while (bits) {
+        const int b = __builtin_ctz(bits);
+        bits &= bits - 1;
+        if (pos >= base && pos < base + kCollectCap) {
+          const int64_t v = slice * TM + (b >> 2) * 16 + 4 * gq + (b & 3);
+          m.buf[pos - base] = cand_key(sr[v], (int)v);
+        }
+        ++pos;
+      }
+    }
+    __syncthreads();
+    const int n = min(kCollectCap, C - base);
+    {
+      uint64_t key[kCollectE];
+#pragma unroll
+      for (int e = 0; e < kCollectE; ++e) {
+        const int jj = wave * (kCollectCap / 4) + e * kWave + lane;
+        key[e] = jj < n ? m.buf[jj] : 0ull;
+      }
+      wave_topk_emit<kCollectE>(key, k, m.tmp[wave], m.ws[wave], m.wi[wave]);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint64_t key[5];
+#pragma unroll
+      for (int e = 0; e < 5; ++e) {
+        const int jj = e * kWave + lane;
+        const int list = jj / k, p = jj - list * k;
+        key[e] = 0ull;
+        if (list < 5) {
+          const int id = m.wi[list][p];
+          if (id != kSentinelId) key[e] = cand_key(m.ws[list][p], id);
+        }
+      }
+      wave_topk_emit<5>(key, k, m.tmp[0], m.ws[4], m.wi[4]);
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < k) {
+    idx[row * k + threadIdx.x] = m.wi[4][threadIdx.x];
+    if (score) score[row * k + threadIdx.x] = m.ws[4][threadIdx.x];
+  }
+}
+
+// ================================================================ launchers
+
+namespace {
+
+using CfgWide = GemmCfg<256, 128, 2, 2>;    // B > 64
+using CfgNarrow = GemmCfg<256, 64, 4, 1>;   // B <= 64
+
+constexpr int kGemmBM = 256;
+
+int64_t vblocks(int64_t V) { return (V + kGemmBM - 1) / kGemmBM; }
+
+int sample_stride(int64_t V, int k) {
+  const int64_t nvb = vblocks(V);
+  int64_t s = nvb * (kGemmBM / 16) / (4 * (int64_t)k);
+  if (s > 8) s = 8;
+  if (s < 1) s = 1;
+  const int64_t lo = (nvb + kMaxSampleTiles / (kGemmBM / 16) - 1) / (kMaxSampleTiles / (kGemmBM / 16));
+  if (s < lo) s = lo;
+  return (int)s;
+}
+
+template <class C>
+size_t gemm_lds_bytes(int K = 1 << 30) {
+  const int nk = (K + kBK - 1) / kBK;
+  return size_t(nk < kStages ? nk : kStages) * (C::BM + C::BN) * kRowChunks * sizeof(u32x4);
+}
+
+template <class C>
+hipError_t allow_lds() {
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_sel_kernel<C, kModeMax>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes<C>());
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)gemm_sel_kernel<C, kModeFilter>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes<C>());
+}
+
+template <class C>
+hipError_t run_gemm(int mode, const uint16_t* M, const uint16_t* X, int64_t V, int K, int64_t B, int nvb,
+                    int stride, float* tmax, int ns_tiles, const float* theta, float* S, int64_t ldS,
+                    uint32_t* mask, int NW, hipStream_t stream) {
+  const int64_t NT = (B + C::BN - 1) / C::BN;
+  const int64_t nvb_pad = (nvb + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid((unsigned)(nvb_pad * NT));
+  const size_t lds = gemm_lds_bytes<C>(K);
+  if (mode == kModeMax)
+    hipLaunchKernelGGL((gemm_sel_kernel<C, kModeMax>), grid, dim3(kGemmThreads), lds, stream, M, X, V, K, B, nvb,
+                       stride, tmax, ns_tiles, theta, S, ldS, mask, NW);
+  else
+    hipLaunchKernelGGL((gemm_sel_kernel<C, kModeFilter>), grid, dim3(kGemmThreads), lds, stream, M, X, V, K, B,
+                       nvb, stride, tmax, ns_tiles, theta, S, ldS, mask, NW);
+  return hipGetLastError();
+}
+
+template <class C>
+hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, int64_t V, int K, int64_t B, int k,
+                    const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream, hipEvent_t ev_before,
+                    hipEvent_t ev_after) {
+  hipError_t e = run_gemm<C>(kModeMax, M, X, V, K, B, p.ns, p.stride, w.tmax, p.ns_tiles, nullptr, nullptr, 0,
+                             nullptr, 0, stream);
+  if (e != hipSuccess) return e;
+  const int cap = min(kWave, k + max(8, k / 4));
+  hipLaunchKernelGGL(theta_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, stream, w.tmax, p.ns_tiles, B, k,
+                     cap, w.theta);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev_before && (e = hipEventRecord(ev_before, stream)) != hipSuccess) return e;
+  e = run_gemm<C>(kModeFilter, M, X, V, K, B, (int)p.nvb, 1, nullptr, 0, w.theta, w.S, p.ldS, w.mask, p.NW,
+                  stream);
+  if (e != hipSuccess) return e;
+  if (ev_after && (e = hipEventRecord(ev_after, stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL(collect_kernel<C::TM>, dim3((unsigned)B), dim3(kGemmThreads), 0, stream, w.mask, p.NW, w.S,
+                     p.ldS, B, k, idx, score);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool batch_path(int dtype, int64_t B) { return dtype == 0 && B > kSmallB; }
+
+hipError_t batch_init() {
+  hipError_t e = allow_lds<CfgWide>();
+  if (e == hipSuccess) e = allow_lds<CfgNarrow>();
+  return e;
+}
+
+BatchPlan plan_batch(int64_t V, int64_t B, int k) {
+  BatchPlan p;
+  p.nvb = vblocks(V);
+  p.stride = sample_stride(V, k);
+  p.ns = (int)((p.nvb + p.stride - 1) / p.stride);
+  p.ns_tiles = p.ns * (kGemmBM / 16);
+  p.ldS = p.nvb * kGemmBM;
+  const int tm = B <= 64 ? CfgNarrow::TM : CfgWide::TM;
+  p.NW = (int)(p.nvb * (kGemmBM / tm) * 4);
+  return p;
+}
+
+size_t batch_scratch_bytes(int64_t V, int64_t B_max) {
+  // sized for the largest of every plan any k and B <= B_max can choose
+  const int64_t nvb = vblocks(V);
+  const size_t tmax = size_t(B_max) * kMaxSampleTiles * 4;
+  const size_t theta = size_t(B_max) * 4;
+  const size_t mask = size_t(B_max) * size_t(nvb) * (kGemmBM / CfgNarrow::TM) * 4 * 4;
+  const size_t S = size_t(B_max) * size_t(nvb) * kGemmBM * 4;
+  auto a = [](size_t x) { return (x + 255) & ~size_t(255); };
+  return a(tmax) + a(theta) + a(mask) + a(S);
+}
+
+BatchScratch batch_scratch(void* base, int64_t V, int64_t B_max) {
+  const int64_t nvb = vblocks(V);
+  auto a = [](size_t x) { return (x + 255) & ~size_t(255); };
+  char* p = static_cast<char*>(base);
+  BatchScratch w;
+  w.tmax = reinterpret_cast<float*>(p);
+  p += a(size_t(B_max) * kMaxSampleTiles * 4);
+  w.theta = reinterpret_cast<float*>(p);
+  p += a(size_t(B_max) * 4);
+  w.mask = reinterpret_cast<uint32_t*>(p);
+  p += a(size_t(B_max) * size_t(nvb) * (kGemmBM / CfgNarrow::TM) * 4 * 4);
+  w.S = reinterpret_cast<float*>(p);
+  return w;
+}
+
+hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, int64_t B, int k,
+                               const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream,
+                               hipEvent_t ev_before, hipEvent_t ev_after) {
+  const BatchPlan p = plan_batch(V, B, k);
+  const uint16_t* m = static_cast<const uint16_t*>(M);
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  if (B <= 64) return run_pass<CfgNarrow>(p, m, x, V, K, B, k, w, idx, score, stream, ev_before, ev_after);
+  return run_pass<CfgWide>(p, m, x, V, K, B, k, w, idx, score, stream, ev_before, ev_after);
+}
+
+}  // namespace lrh

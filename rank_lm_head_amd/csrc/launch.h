@@ -45,6 +45,39 @@ hipError_t launch_select(int dtype, const void* M, const void* X, int64_t V, int
 hipError_t launch_dense(int dtype, const void* W, const void* H, int64_t V, int d, int64_t B,
                         float* logits, hipStream_t stream);
 
+// ------------------------------------------------------ kernels_gemm.hip
+// bf16 row batches (B > kSmallB) take the matrix-core GEMM with a sampled
+// per-row bound and an exact collect (no per-slice lists).
+bool batch_path(int dtype, int64_t B);
+
+struct BatchPlan {
+  int64_t nvb;      // vocabulary blocks of 256 rows
+  int stride;       // sample pass: every stride-th block
+  int ns;           // sampled blocks
+  int ns_tiles;     // tile maxima per row (ns * 16 <= 2048)
+  int64_t ldS;      // row stride of the sparse score array (nvb * 256)
+  int NW;           // mask words per row
+};
+BatchPlan plan_batch(int64_t V, int64_t B, int k);
+
+struct BatchScratch {
+  float* tmax;      // B_max x 2048 tile maxima
+  float* theta;     // B_max per-row bounds
+  uint32_t* mask;   // B_max x NW flags
+  float* S;         // B_max x ldS sparse scores
+};
+size_t batch_scratch_bytes(int64_t V, int64_t B_max);
+BatchScratch batch_scratch(void* base, int64_t V, int64_t B_max);
+// Lets the GEMM kernels use more than 64 KiB of LDS (call once per device).
+hipError_t batch_init();
+
+// The k best of every row of X . M^T (M is V x K, X is B x K, bf16) in
+// candidate order to idx / score (score may be NULL). Events, when given,
+// are recorded around the main GEMM pass.
+hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, int64_t B, int k,
+                               const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream,
+                               hipEvent_t ev_before, hipEvent_t ev_after);
+
 // ----------------------------------------------------- kernels_merge.hip
 // Merges n sorted lists of k per row (part_[row][list][k], n <= 512) into
 // idx / score (score may be NULL). With logits != NULL, also writes the

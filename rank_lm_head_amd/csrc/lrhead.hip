@@ -28,6 +28,8 @@ struct lrhead_s {
   void* z;          // B_max x r, weight dtype
   float* part_s;    // candidate lists: rows x slices x k_max
   int* part_i;
+  bool batch;       // bf16 with B_max > 4: the GEMM path's scratch exists
+  lrh::BatchScratch bw;
   hipEvent_t ev_before;  // optional events around the selection kernel
   hipEvent_t ev_after;
 };
@@ -56,7 +58,7 @@ size_t elem_bytes(int dtype) { return dtype == LRHEAD_BF16 ? 2 : 4; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t z, part_s, part_i, total;
+  size_t z, part_s, part_i, batch, total;
 };
 
 // Most candidate lists any call with B <= B_max writes (B x slices), over
@@ -81,7 +83,9 @@ Layout layout(int dtype, int64_t V, int64_t r, int64_t B_max, int k_max) {
   const size_t lists = align256(size_t(max_list_rows(B_max, V)) * size_t(k_max) * 4);
   L.part_s = zb;
   L.part_i = zb + lists;
-  L.total = zb + 2 * lists;
+  L.batch = zb + 2 * lists;
+  L.total = L.batch;
+  if (lrh::batch_path(dtype, B_max)) L.total += align256(lrh::batch_scratch_bytes(V, B_max));
   return L;
 }
 
@@ -141,6 +145,15 @@ int record(hipEvent_t ev, hipStream_t s) {
 // the slice lists; with `logits`, the merge also rescores the winners.
 int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, float* score, float* logits,
                  hipStream_t s) {
+  if (lrh::batch_path(h->dtype, B)) {
+    LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
+    LRH_HIP(lrh::launch_batch_select(h->P, h->z, h->V, (int)h->r, B, k, h->bw, idx, score, s, h->ev_before,
+                                     h->ev_after),
+            "score/selection launch");
+    if (logits)
+      LRH_HIP(lrh::launch_rescore(h->dtype, h->W, H, idx, B, k, h->V, (int)h->d, logits, s), "rescore launch");
+    return LRHEAD_OK;
+  }
   int n_lists;
   if (lrh::small_path(h->dtype, B, h->r, h->V)) {
     LRH_HIP(lrh::launch_down_small(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
@@ -192,6 +205,8 @@ int lrhead_create(lrhead_t* out, int dtype, int64_t V, int64_t d, int64_t r, con
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(LRHEAD_EDEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
 
+  if (lrh::batch_path(dtype, B_max)) LRH_HIP(lrh::batch_init(), "GEMM kernel set-up");
+
   lrhead_s* h = new (std::nothrow) lrhead_s;
   if (!h) return fail(LRHEAD_EINVAL, "out of host memory");
   h->magic = kMagic;
@@ -209,6 +224,8 @@ int lrhead_create(lrhead_t* out, int dtype, int64_t V, int64_t d, int64_t r, con
   h->z = h->ws + L.z;
   h->part_s = reinterpret_cast<float*>(h->ws + L.part_s);
   h->part_i = reinterpret_cast<int*>(h->ws + L.part_i);
+  h->batch = lrh::batch_path(dtype, B_max);
+  h->bw = h->batch ? lrh::batch_scratch(h->ws + L.batch, V, B_max) : lrh::BatchScratch{};
   h->ev_before = nullptr;
   h->ev_after = nullptr;
   *out = h;
@@ -250,6 +267,12 @@ int fullhead_topk(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, flo
   LRH_TRY(check_out(logits, "logits", B > 0));
   if (B == 0) return LRHEAD_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (lrh::batch_path(h->dtype, B)) {
+    LRH_HIP(lrh::launch_batch_select(h->W, H, h->V, (int)h->d, B, k, h->bw, idx, logits, s, h->ev_before,
+                                     h->ev_after),
+            "full-head selection launch");
+    return LRHEAD_OK;
+  }
   int n_lists;
   if (lrh::small_long_path(h->dtype, B, h->d, h->V)) {
     n_lists = lrh::small_blocks(h->V);

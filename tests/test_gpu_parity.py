@@ -117,6 +117,47 @@ def test_streaming_path_shapes(V, d, r, B, k):
     say(f"[ok] {stats}")
 
 
+@pytest.mark.parametrize("V,d,r,B,k", [
+    (20000, 256, 96, 130, 48),   # wide batch tile: two row tiles, the second ragged; K tail of 32
+    (6000, 384, 256, 64, 64),    # narrow batch tile exactly full, k = 64
+    (12345, 200, 72, 65, 10),    # one row past the narrow tile; K = 64 + 8
+    (257, 64, 16, 9, 9),         # two vocabulary blocks, the second holding one row
+])
+def test_batch_path_shapes(V, d, r, B, k):
+    inp = gen.make_custom(V, d, r, B, "bf16", seed=V + B)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=k)
+    say(f"[run] batch V={V} d={d} r={r} B={B} k={k}")
+    idx, score, lg = head.draft(t["H"], k)
+    fidx, flog = head.full_topk(t["H"], k)
+    torch.cuda.synchronize()
+    errs, stats = check_lowrank(inp, k, np_(idx), np_(score), np_(lg))
+    assert not errs, errs[:5]
+    errs, _ = check_full(inp, k, np_(fidx), np_(flog))
+    assert not errs, errs[:5]
+    say(f"[ok] {stats}")
+
+
+def test_batch_duplicate_rows_tie_to_the_lower_id():
+    """Bitwise-equal vocabulary rows in different vocabulary blocks: the
+    batch path returns them in id order (8 draft rows)."""
+    V, B = 3000, 8
+    inp = gen.make_custom(V, 128, 32, B, "bf16", seed=15)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=4)
+    tok = int(np_(head.candidates(t["H"], 1)[0])[0, 0])
+    assume = tok not in (0, V - 1)
+    if not assume:
+        pytest.skip("row 0's best token sits at an end of the vocabulary")
+    P2 = t["P"].clone()
+    for dst in (0, V - 1):
+        P2[dst] = t["P"][tok]
+    h2 = lr.Head(t["Q"], P2, t["W"], B_max=B, k_max=4)
+    idx, score = h2.candidates(t["H"], 3)
+    assert np_(idx)[0].tolist() == [0, tok, V - 1]
+    assert len(set(np_(score)[0].tolist())) == 1
+
+
 @pytest.mark.parametrize("B", [1, 8])
 def test_all_scores_tied(B):
     """Every score equal: the k lowest ids win, in order (forces the merge's
