@@ -37,10 +37,11 @@ if ROOT not in sys.path:
 
 METRIC = "draft-head µs/call & rows/s at V=151936,d=5120,r=128; % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense matrix peaks
 MALL_BYTES = 256 << 20
 BENCH_CONFIG = 2
 KERNEL_SOURCES = ["rank_lm_head_amd/csrc/kernels_small.hip", "rank_lm_head_amd/csrc/kernels_mfma.hip",
+                  "rank_lm_head_amd/csrc/kernels_gemm.hip",
                   "rank_lm_head_amd/csrc/kernels_merge.hip", "rank_lm_head_amd/csrc/topk.h",
                   "rank_lm_head_amd/csrc/device.h"]
 
@@ -267,14 +268,34 @@ def main() -> int:
     us_full = t_full / ((KB + 3) // 4 * 4) * 1e6
     full_sel_s = event_timed(torch, hip, heads[:1], full, min(KB, 200))
 
-    # roofline of the dominant kernel: the vocabulary score/selection pass.
-    # Algorithmic bytes per launch: every P row once (V units of r*s bytes)
-    # plus the B rows of z.
+    # roofline of the dominant kernel: the vocabulary score pass. Algorithmic
+    # work per launch: every P row once (V units of r*s bytes) plus the B rows
+    # of z, and 2*B*r flops per vocabulary row. Small batches stream P on the
+    # vector ALU (HBM-bound); row batches run the matrix-core GEMM, which is
+    # bound by whichever of HBM and MFMA its arithmetic intensity points to.
     sel_bytes = cfg.V * cfg.r * s + cfg.B * cfg.r * s
-    sel_gbs = sel_bytes / sel_s / 1e9
+    sel_flops = 2.0 * cfg.B * cfg.V * cfg.r
+    batch = cfg.dtype == "bf16" and cfg.B > 4
     small = cfg.dtype == "bf16" and cfg.B <= 4 and cfg.r in (8, 16, 32, 64, 128, 256, 512)
-    sel_kernel = "select_short_kernel" if small else "select_mfma_kernel"
+    if batch:
+        sel_kernel, what = "gemm_sel_kernel", "main GEMM pass: scores of all rows, flagged above the sampled bound"
+    elif small:
+        sel_kernel, what = "select_short_kernel", "score pass + per-slice top-k"
+    else:
+        sel_kernel, what = "select_mfma_kernel", "score pass + per-slice top-k"
+    peak_flops = MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12
+    mfma_bound = sel_flops / sel_bytes > peak_flops / (HBM_PEAK_GBS * 1e9)
     traffic = traffic_from_profiles(sel_kernel, f"c{cid}")
+    if mfma_bound:
+        roof = {"bound": "mfma", "kernel": f"{sel_kernel} ({what})",
+                "achieved": sel_flops / sel_s / 1e12, "peak": peak_flops / 1e12, "unit": "TFLOP/s",
+                "frac": sel_flops / sel_s / peak_flops, "traffic": traffic,
+                "us_per_launch": sel_s * 1e6, "flops_per_launch": sel_flops, "bytes_per_launch": sel_bytes}
+    else:
+        roof = {"bound": "hbm", "kernel": f"{sel_kernel} ({what})",
+                "achieved": sel_bytes / sel_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": sel_bytes / sel_s / (HBM_PEAK_GBS * 1e9), "traffic": traffic,
+                "us_per_launch": sel_s * 1e6, "bytes_per_launch": sel_bytes}
     call_bytes = (cfg.r * cfg.d + cfg.V * cfg.r + cfg.B * cfg.d + U * cfg.d) * s + cfg.B * cfg.k * 12
     call_flops = 2.0 * cfg.B * (cfg.r * cfg.d + cfg.V * cfg.r + cfg.k * cfg.d)
     full_bytes = cfg.V * cfg.d * s + cfg.B * cfg.d * s
@@ -301,13 +322,11 @@ def main() -> int:
         "call_bytes": call_bytes,
         "call_flops": call_flops,
         "distinct_W_rows": U,
-        "roofline": {"bound": "hbm", "kernel": f"{sel_kernel} (score pass + per-slice top-k)",
-                     "achieved": sel_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": sel_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "us_per_launch": sel_s * 1e6, "bytes_per_launch": sel_bytes},
+        "roofline": roof,
         "full_head": {"us_per_call": us_full, "speedup_of_draft_head": us_full / us_cold,
                       "select_us_per_launch": full_sel_s * 1e6,
-                      "hbm_frac": full_bytes / (full_sel_s) / (HBM_PEAK_GBS * 1e9)},
+                      "hbm_frac": full_bytes / (full_sel_s) / (HBM_PEAK_GBS * 1e9),
+                      "mfma_frac": 2.0 * cfg.B * cfg.V * cfg.d / full_sel_s / peak_flops},
     }
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20

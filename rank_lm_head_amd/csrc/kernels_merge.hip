@@ -10,9 +10,9 @@
 // Merge. Take any bound T that at least k list heads (best entries) reach.
 // Then at least k entries reach T, so an entry below T is preceded by k
 // others and cannot win, and a list whose head is below T holds no winner.
-// Wave 0 finds a T that between k and 64 heads reach (windowed bisection,
-// topk.h), the block collects the entries of those active lists that reach
-// T (a few k of them), and wave 0 ranks the k best of those.
+// The kernel reads all lists of a row in one coalesced pass, finds such a T
+// among the heads (windowed bisection, topk.h), gathers the entries that
+// reach it (a few k of them) and ranks the k best of those.
 //
 // Rescoring: logit = W[id, :] . h with fp32 accumulation, one wave per
 // candidate, every load of the W row and of h issued before the products.
@@ -86,25 +86,76 @@ __global__ void __launch_bounds__(256) rescore_kernel(const T* __restrict__ W, c
 }
 
 // ---------------------------------------------------------------- merge
-constexpr int kHeadE = kMaxLists / kWave;   // heads per lane of wave 0
 constexpr int kCandE = 8;                   // candidates per lane of wave 0
 constexpr int kCandSlots = kCandE * kWave;
+constexpr int kHeadE = kMaxLists / kWave;   // list heads per lane of wave 0
+constexpr int kFront = 4;                   // leading entries of each list read up front
 
 struct MergeSmem {
+  uint64_t heads[kMaxLists];
   uint64_t cand[kCandSlots];
+  float spec[kCandSlots];   // exact logit of candidate slot j (this block's share)
+  int slot_of[kWave];       // candidate slot of each winner
   uint64_t tmp[kWave];
-  int active[kWave];
+  int tslot[kWave];
   float top_s[kWave];
   int top_i[kWave];
+  int deep[kMaxLists];       // lists whose front entries all reach the bound
   uint64_t T;
-  int n_active;
   int n_cand;
+  int n_deep;
 };
 
-// Grid (G, B): block (g, b) merges row b's n lists (list p at
-// part + (b*n + p)*k) and, with RESCORE, rescores the winners g*per ..
-// g*per+per-1 (per = ceil(k/G), one wave each). Block g == 0 writes idx and
-// score. All G blocks of a row compute the same winners.
+// The k best of the n_cand candidate keys in m.cand, in candidate order, to
+// m.top_s / m.top_i (wave 0), and m.slot_of[rank] = the winner's slot.
+__device__ __forceinline__ void select_candidates(MergeSmem& m, int nc, int k) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[kCandE];
+#pragma unroll
+  for (int e = 0; e < kCandE; ++e) {
+    const int j = e * kWave + lane;
+    key[e] = j < nc ? m.cand[j] : 0ull;
+  }
+  const uint64_t T = wave_window_threshold<kCandE>(key, k, kWave);
+  int n = 0;
+#pragma unroll
+  for (int e = 0; e < kCandE; ++e) {
+    const bool sel = key[e] != 0 && key[e] >= T;
+    const unsigned long long mk = __ballot(sel);
+    if (sel) {
+      const int p = n + lanes_below(mk);
+      if (p < kWave) {
+        m.tmp[p] = key[e];
+        m.tslot[p] = e * kWave + lane;
+      }
+    }
+    n += __popcll(mk);
+  }
+  n = min(n, kWave);
+  pad_keys(m.tmp, n);
+  const int slot = lane < n ? m.tslot[lane] : 0;
+  const int r = wave_rank_emit(m.tmp, n, k, m.top_s, m.top_i);
+  if (lane < n && r < k) m.slot_of[r] = slot;
+}
+
+// Grid (G, B), 512 threads: block (g, b) merges row b's n lists (sorted,
+// depth-major: entry j of list p at part + (b * k + j) * n + p) and, with
+// RESCORE, gives the winners their exact logits. All G blocks of a row
+// compute the same winners; block 0 writes idx and score.
+//  1. The first 4 entries of every list are read in one coalesced pass (one
+//     list per thread) and the heads go to LDS.
+//  2. Wave 0 finds a bound T that between k and k + k/4 + 4 heads reach;
+//     every thread sends its front entries that reach T to the candidate
+//     buffer. Only a list whose 4th entry still reaches T can hold more
+//     candidates; those (rare) lists are read further, one per wave.
+//  3. Wave 0 ranks the candidates. Meanwhile, when there are few enough
+//     candidates, waves 1..7 of the G blocks already compute the logits of
+//     all of them, so the W rows are in flight during the selection: a
+//     candidate with token id v belongs to block v % G (the blocks' buffers
+//     hold the same candidates in different orders, the ids agree), and the
+//     block's waves take its candidates in turn. Afterwards each block
+//     writes the logits of the winners that belong to it. With more
+//     candidates, wave w of block g rescores winner g*per + w instead.
 template <typename T, bool RESCORE>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
     const float* __restrict__ part_s, const int* __restrict__ part_i, int n, int64_t V, int k,
@@ -113,104 +164,162 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
   __shared__ MergeSmem m;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t b = blockIdx.y;
-  const float* ps = part_s + b * n * k;
-  const int* pi = part_i + b * n * k;
+  const int G = gridDim.x, g = blockIdx.x;
 
-  // 1. a bound T that between k and 64 heads reach (wave 0); the lists whose head reaches T
-  if (wave == 0) {
-    // all loads first, from clamped (valid) addresses, then the keys
-    float hs[kHeadE];
-    int hid[kHeadE];
+  // 1. the first kFront entries of every list (contiguous across lists in
+  //    the depth-major layout), one list per thread; heads to LDS
+  const int64_t R = b * (int64_t)k * n;   // row base
+  const int p = threadIdx.x;
+  const int pc = min(p, n - 1);
+  float fs[kFront];
+  int fi[kFront];
 #pragma unroll
-    for (int e = 0; e < kHeadE; ++e) {
-      const int p = min(e * kWave + lane, n - 1);
-      hs[e] = ps[(int64_t)p * k];
-      hid[e] = pi[(int64_t)p * k];
-    }
+  for (int j = 0; j < kFront; ++j) {
+    const int jc = min(j, k - 1);
+    fs[j] = part_s[R + (int64_t)jc * n + pc];
+    fi[j] = part_i[R + (int64_t)jc * n + pc];
+    if (p >= n || j >= k) fi[j] = kSentinelId;
+  }
+  if (p < n) m.heads[p] = fi[0] != kSentinelId ? cand_key(fs[0], fi[0]) : 0ull;
+  if (threadIdx.x == 0) {
+    m.n_cand = 0;
+    m.n_deep = 0;
+  }
+  __syncthreads();
+
+  // 2. the bound, then the candidates
+  if (wave == 0) {
     uint64_t key[kHeadE];
 #pragma unroll
-    for (int e = 0; e < kHeadE; ++e)
-      key[e] = (e * kWave + lane < n && hid[e] != kSentinelId) ? cand_key(hs[e], hid[e]) : 0ull;
-    const uint64_t T1 = wave_window_threshold<kHeadE>(key, k, kWave);
-    int na = 0;
-#pragma unroll
     for (int e = 0; e < kHeadE; ++e) {
-      const bool act = key[e] != 0 && key[e] >= T1;
-      const unsigned long long mk = __ballot(act);
-      if (act) m.active[na + lanes_below(mk)] = e * kWave + lane;
-      na += __popcll(mk);
+      const int q = e * kWave + lane;
+      key[e] = q < n ? m.heads[q] : 0ull;
     }
-    if (lane == 0) {
-      m.T = T1;
-      m.n_active = na;
-      m.n_cand = 0;
-    }
+    const uint64_t T1 = wave_window_threshold<kHeadE>(key, k, min(kWave, k + k / 4 + 4));
+    if (lane == 0) m.T = T1;
   }
   __syncthreads();
-
-  // 2. entries of the active lists that reach T; wave w takes active lists
-  //    w, w+8, ... (at most 8 of them), all loads issued first
+  // The bound as (score, id): key >= T1 holds when the score is larger, or
+  // equal with (unsigned) id <= 0xFFFFFFFF - low word of T1 (every id when
+  // the bound came from the window, whose low word is 0).
+  const uint64_t T1 = m.T;
+  const float ts = key_score(T1);
+  const uint32_t tid = 0xFFFFFFFFu - (uint32_t)T1;
+  const bool all = T1 == 1;   // every non-empty entry counts
+  auto reaches = [&](float sc, int id) {
+    sc = sc + 0.0f;
+    return id != kSentinelId && (all || sc > ts || (sc == ts && (uint32_t)id <= tid));
+  };
   {
-    const uint64_t T1 = m.T;
-    const int na = m.n_active;
-    constexpr int kPerWave = kWave / kMergeWaves;
-    const int j = min(lane, k - 1);
-    float es[kPerWave];
-    int ei[kPerWave];
+    uint32_t pass = 0;
 #pragma unroll
-    for (int q = 0; q < kPerWave; ++q) {
-      const int a = wave + q * kMergeWaves;
-      const int p = a < na ? m.active[a] : 0;
-      es[q] = ps[(int64_t)p * k + j];
-      ei[q] = pi[(int64_t)p * k + j];
+    for (int j = 0; j < kFront; ++j) pass |= (reaches(fs[j], fi[j]) ? 1u : 0u) << j;
+    // slots from a prefix over the wave's lanes of their counts (bit planes)
+    const int cnt = __popc(pass);
+    int before = 0, wave_total = 0;
+#pragma unroll
+    for (int bit = 0; bit < 3; ++bit) {
+      const unsigned long long plane = __ballot((cnt >> bit) & 1);
+      before += lanes_below(plane) << bit;
+      wave_total += __popcll(plane) << bit;
     }
-#pragma unroll
-    for (int q = 0; q < kPerWave; ++q) {
-      if (wave + q * kMergeWaves >= na) break;
-      const uint64_t key = (lane < k && ei[q] != kSentinelId) ? cand_key(es[q], ei[q]) : 0ull;
-      const bool pass = key != 0 && key >= T1;
-      const unsigned long long mk = __ballot(pass);
-      int base = 0;
-      if (lane == 0 && mk) base = atomicAdd(&m.n_cand, __popcll(mk));
+    int base = 0;
+    if (wave_total) {
+      if (lane == 0) base = atomicAdd(&m.n_cand, wave_total);
       base = __shfl(base, 0);
-      const int slot = base + lanes_below(mk);
-      if (pass && slot < kCandSlots) m.cand[slot] = key;
     }
+    int slot = base + before;
+#pragma unroll
+    for (int j = 0; j < kFront; ++j) {
+      if (pass & (1u << j)) {
+        if (slot < kCandSlots) m.cand[slot] = cand_key(fs[j], fi[j]);
+        ++slot;
+      }
+    }
+    // a list whose last front entry reaches the bound may hold more
+    if (k > kFront && (pass >> (kFront - 1)) & 1u) m.deep[atomicAdd(&m.n_deep, 1)] = p;
   }
   __syncthreads();
-
-  // 3. the k best candidates, in order (wave 0)
-  if (wave == 0) {
-    const int nc = m.n_cand;
-    if (nc <= kCandSlots) {
-      uint64_t key[kCandE];
-#pragma unroll
-      for (int e = 0; e < kCandE; ++e) {
-        const int j = e * kWave + lane;
-        key[e] = j < nc ? m.cand[j] : 0ull;
+  if (m.n_deep > 0) {
+    // rare: the rest of those lists, one list per wave at a time
+    const int nd = m.n_deep;
+    for (int dl = wave; dl < nd; dl += kMergeWaves) {
+      const int q = m.deep[dl];
+      const int j = kFront + lane;
+      const int jc = min(j, k - 1);
+      const float sc = part_s[R + (int64_t)jc * n + q];
+      const int id = j < k ? part_i[R + (int64_t)jc * n + q] : kSentinelId;
+      const bool ps = reaches(sc, id);
+      const unsigned long long mk = __ballot(ps);
+      if (mk) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&m.n_cand, __popcll(mk));
+        base = __shfl(base, 0);
+        const int slot = base + lanes_below(mk);
+        if (ps && slot < kCandSlots) m.cand[slot] = cand_key(sc, id);
       }
-      wave_topk_emit<kCandE>(key, k, m.tmp, m.top_s, m.top_i);
+    }
+    __syncthreads();
+  }
+  const int nc = m.n_cand;
+
+  // 3. selection, with the rescoring in flight when it can be
+  const bool fits = nc <= kCandSlots;
+  const bool spec = RESCORE && fits && nc <= G * (kMergeWaves - 1);
+  if (wave == 0) {
+    if (fits) {
+      select_candidates(m, nc, k);
     } else {
       float s;
       int i;
-      merge_lists_seq(ps, pi, n, k, s, i);
+      merge_lists_seq(part_s + R, part_i + R, n, k, s, i);
       m.top_s[lane] = s;
       m.top_i[lane] = i;
     }
-    if (blockIdx.x == 0 && lane < k) {
-      idx[b * k + lane] = m.top_i[lane];
-      if (score) score[b * k + lane] = m.top_s[lane];
+  } else if (spec) {
+    // this block's candidates in slot order; the t-th goes to wave 1 + t % 7
+    int seen = 0;
+    for (int base = 0; base < nc; base += kWave) {
+      const int j = base + lane;
+      const bool own = j < nc && key_id(m.cand[j]) % G == g;
+      const unsigned long long mk = __ballot(own);
+      const bool take = own && (seen + lanes_below(mk)) % (kMergeWaves - 1) == wave - 1;
+      unsigned long long mt = __ballot(take);
+      while (mt) {
+        const int jj = base + __builtin_ctzll(mt);
+        mt &= mt - 1;
+        const int v = key_id(m.cand[jj]);
+        const float x = (v >= 0 && v < V) ? wave_row_dot<T>(W + (int64_t)v * d, H + b * (int64_t)d, d)
+                                          : __builtin_nanf("");
+        if (lane == 0) m.spec[jj] = x;
+      }
+      seen += __popcll(mk);
     }
   }
+  __syncthreads();
+  if (g == 0 && wave == 0 && lane < k) {
+    idx[b * k + lane] = m.top_i[lane];
+    if (score) score[b * k + lane] = m.top_s[lane];
+  }
   if constexpr (RESCORE) {
-    __syncthreads();
-    const int per = (k + gridDim.x - 1) / gridDim.x;
-    const int j = blockIdx.x * per + wave;
-    if (wave < per && j < k) {
-      const int v = m.top_i[j];
-      float acc = __builtin_nanf("");
-      if (v >= 0 && v < V) acc = wave_row_dot<T>(W + (int64_t)v * d, H + b * (int64_t)d, d);
-      if (lane == 0) logits[b * k + j] = acc;
+    if (spec) {
+      if (threadIdx.x < k) {
+        const int r = threadIdx.x, v = m.top_i[r];
+        if (v == kSentinelId) {
+          if (g == 0) logits[b * k + r] = __builtin_nanf("");   // fewer than k candidates
+        } else if (v % G == g) {
+          logits[b * k + r] = m.spec[m.slot_of[r]];
+        }
+      }
+    } else {
+      const int per = (k + G - 1) / G;
+      const int j = g * per + wave;
+      if (wave < per && j < k) {
+        const int v = m.top_i[j];
+        float acc = __builtin_nanf("");
+        if (v >= 0 && v < V) acc = wave_row_dot<T>(W + (int64_t)v * d, H + b * (int64_t)d, d);
+        if (lane == 0) logits[b * k + j] = acc;
+      }
     }
   }
 }
@@ -234,19 +343,22 @@ hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n
                         int64_t B, int k, const void* W, const void* H, int d, int32_t* idx, float* score,
                         float* logits, hipStream_t stream) {
   if (n < 1 || n > kMaxLists) return hipErrorInvalidValue;
+  const dim3 block(kMergeThreads);
   if (!logits) {
-    dim3 grid(1, (unsigned)B);
-    hipLaunchKernelGGL((merge_kernel<uint16_t, false>), grid, dim3(kMergeThreads), 0, stream, part_s, part_i, n,
-                       V, k, (const uint16_t*)nullptr, (const uint16_t*)nullptr, d, idx, score, logits);
+    const dim3 grid(1, (unsigned)B);
+    hipLaunchKernelGGL((merge_kernel<uint16_t, false>), grid, block, 0, stream, part_s, part_i, n, V, k,
+                       (const uint16_t*)nullptr, (const uint16_t*)nullptr, d, idx, score, logits);
     return hipGetLastError();
   }
-  dim3 grid((unsigned)((k + kMergeWaves - 1) / kMergeWaves), (unsigned)B);
+  // enough blocks that waves 1..7 of all of them can hold 2k candidates
+  const int G = (2 * k + kMergeWaves - 2) / (kMergeWaves - 1);
+  const dim3 grid((unsigned)G, (unsigned)B);
   if (dtype == 0)
-    hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, dim3(kMergeThreads), 0, stream, part_s, part_i, n,
-                       V, k, (const uint16_t*)W, (const uint16_t*)H, d, idx, score, logits);
+    hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, block, 0, stream, part_s, part_i, n, V, k,
+                       (const uint16_t*)W, (const uint16_t*)H, d, idx, score, logits);
   else
-    hipLaunchKernelGGL((merge_kernel<float, true>), grid, dim3(kMergeThreads), 0, stream, part_s, part_i, n,
-                       V, k, (const float*)W, (const float*)H, d, idx, score, logits);
+    hipLaunchKernelGGL((merge_kernel<float, true>), grid, block, 0, stream, part_s, part_i, n, V, k,
+                       (const float*)W, (const float*)H, d, idx, score, logits);
   return hipGetLastError();
 }
 

@@ -132,7 +132,7 @@ __device__ __forceinline__ void fold_column(TileSel& st, int n, int k, float& th
 // Grid: (n_vsplit, ceil(B/16)). Block (split, bt) handles rows b0..b0+15 and
 // the split's contiguous run of 16-row vocabulary tiles; wave w takes tiles
 // w, w+4, ... Each wave keeps its own per-column lists; the four are merged
-// at the end and the k best go to part_[row][split].
+// at the end and the k best go to part_[row][entry][split].
 template <typename T>
 __global__ void __launch_bounds__(256) select_mfma_kernel(const T* __restrict__ M, const T* __restrict__ X,
                                                           int64_t V, int K, int64_t B, int k, int n_vsplit,
@@ -202,7 +202,7 @@ __global__ void __launch_bounds__(256) select_mfma_kernel(const T* __restrict__ 
     for (int w = 1; w < kWaves; ++w)
       merge_reversed(s, i, sel[w].ls[n][kWave - 1 - lane], sel[w].li[n][kWave - 1 - lane]);
     if (lane < k) {
-      const int64_t o = ((b0 + n) * n_vsplit + split) * k + lane;
+      const int64_t o = ((b0 + n) * k + lane) * n_vsplit + split;
       part_s[o] = s;
       part_i[o] = i;
     }

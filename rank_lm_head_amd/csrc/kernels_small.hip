@@ -60,7 +60,7 @@ __global__ void __launch_bounds__(kSmallThreads) down_small_kernel(const uint16_
 
 // ------------------------------------------------- shared tail of the pass
 // Each wave hands its per-row lists to LDS; wave b merges the four lists of
-// row b and writes the block's sorted list to part_[b][block][0..k).
+// row b and writes the block's sorted list: entry j to part_[b][j][block].
 template <int NB>
 struct SmallLds {
   float bs[kWavesSmall][NB][kBuf];
@@ -90,7 +90,7 @@ __device__ __forceinline__ void finish_block(SmallLds<NB>& sm, WaveSel<NB>& st, 
     for (int w = 1; w < kWavesSmall; ++w)
       merge_reversed(s, i, sm.cs[w][b][kWave - 1 - lane], sm.ci[w][b][kWave - 1 - lane]);
     if (lane < k) {
-      const int64_t o = ((int64_t)b * nblk + blockIdx.x) * k + lane;
+      const int64_t o = ((int64_t)b * k + lane) * nblk + blockIdx.x;
       part_s[o] = s;
       part_i[o] = i;
     }
@@ -104,7 +104,8 @@ __device__ __forceinline__ void finish_block(SmallLds<NB>& sm, WaveSel<NB>& st, 
 // it; the next U wave loads are issued before the current ones are used.
 // The scores go to LDS, and after the pass wave b finds the k best of the
 // slice for row b (windowed bisection and counting ranks, topk.h) and writes
-// them, in order, to part_[b][x][0..k).
+// them, in order: entry j to part_[b][j][x] (depth-major, so that the first
+// entries of all lists are contiguous for the merge).
 constexpr int kBlockRows = 512;
 
 template <int K, int NB, int E>
@@ -170,8 +171,8 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
       const int j = e * kWave + lane;
       key[e] = j < nrows ? cand_key(sc[b][j], (int)(blo + j)) : 0ull;
     }
-    const int64_t o = ((int64_t)b * nblk + blockIdx.x) * k;
-    wave_topk_emit<E>(key, k, tmp[b], part_s + o, part_i + o);
+    const int64_t o = (int64_t)b * k * nblk + blockIdx.x;
+    wave_topk_emit<E>(key, k, tmp[b], part_s + o, part_i + o, nblk);
   }
 }
 

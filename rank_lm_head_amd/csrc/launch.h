@@ -21,7 +21,7 @@ bool small_long_path(int dtype, int64_t B, int64_t K, int64_t V);
 // z = round(Q . h) for B <= 4 rows.
 hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream);
 // Streaming score pass: per block, the k best of its slice for each row,
-// written to part_[row][block][0..k).
+// written depth-major: entry j of block x's list at part_[row][j][x].
 hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
                                int* part_i, hipStream_t stream);
 hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
@@ -37,7 +37,7 @@ hipError_t launch_down(int dtype, const void* Q, const void* H, int r, int d, in
                        void* Z, hipStream_t stream);
 
 // Per-slice candidate lists of "M . x" for B rows: M is V x K (P or W),
-// X is B x K (z or h). Writes part_s / part_i: [B][n_vsplit][k].
+// X is B x K (z or h). Writes part_s / part_i: [B][k][n_vsplit].
 hipError_t launch_select(int dtype, const void* M, const void* X, int64_t V, int K, int64_t B,
                          int k, int n_vsplit, float* part_s, int* part_i, hipStream_t stream);
 
@@ -79,7 +79,7 @@ hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, i
                                hipEvent_t ev_before, hipEvent_t ev_after);
 
 // ----------------------------------------------------- kernels_merge.hip
-// Merges n sorted lists of k per row (part_[row][list][k], n <= 512) into
+// Merges n sorted lists of k per row (part_[row][entry][list], n <= 512) into
 // idx / score (score may be NULL). With logits != NULL, also writes the
 // winners' exact logits W[id] . h_b.
 hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int64_t V, int64_t B, int k,

@@ -80,7 +80,8 @@ Layout layout(int dtype, int64_t V, int64_t r, int64_t B_max, int k_max) {
   Layout L;
   L.z = 0;
   const size_t zb = align256(size_t(B_max) * size_t(r) * elem_bytes(dtype));
-  const size_t lists = align256(size_t(max_list_rows(B_max, V)) * size_t(k_max) * 4);
+  // the merge reads whole 16-byte chunks, up to 12 bytes past the last list
+  const size_t lists = align256(size_t(max_list_rows(B_max, V)) * size_t(k_max) * 4 + 16);
   L.part_s = zb;
   L.part_i = zb + lists;
   L.batch = zb + 2 * lists;

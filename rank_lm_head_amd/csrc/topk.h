@@ -16,8 +16,8 @@
 //    to LDS and each is placed by counting the keys that precede it, which
 //    orders them as well (no sorting network on the hot path).
 //
-//  * wave_select_threshold / wave_emit_sorted: the exact k-th best by a
-//    full bisection, used when ties keep the window from being reached.
+//  * wave_select_threshold: the exact k-th best by a full bisection, used
+//    when ties keep the window from being reached.
 //
 //  * merge_lists_seq: a wave-wide fold of sorted lists, the fallback of the
 //    merge kernel when too many entries tie at its threshold.
@@ -105,24 +105,28 @@ __device__ __forceinline__ int key_id(uint64_t key) { return (int)(0xFFFFFFFFu -
 
 __device__ __forceinline__ int wave_count(bool p) { return __popcll(__ballot(p)); }
 
-// Wave-wide min / max of a 32-bit value.
+// Wave-wide min / max of a 32-bit value: DPP inside each row of 16 lanes
+// (pairs, quads, half rows, rows), then the four row results by readlane.
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, Ctrl, 0xf, 0xf, true);
+}
+__device__ __forceinline__ uint32_t rl(uint32_t x, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-  x = min(x, (uint32_t)lane_xor<1>((int)x));
-  x = min(x, (uint32_t)lane_xor<2>((int)x));
-  x = min(x, (uint32_t)lane_xor<4>((int)x));
-  x = min(x, (uint32_t)lane_xor<8>((int)x));
-  x = min(x, (uint32_t)lane_xor<16>((int)x));
-  x = min(x, (uint32_t)lane_xor<32>((int)x));
-  return x;
+  x = min(x, dpp_u32<0xB1>(x));
+  x = min(x, dpp_u32<0x4E>(x));
+  x = min(x, dpp_u32<0x141>(x));
+  x = min(x, dpp_u32<0x140>(x));
+  return min(min(rl(x, 0), rl(x, 16)), min(rl(x, 32), rl(x, 48)));
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-  x = max(x, (uint32_t)lane_xor<1>((int)x));
-  x = max(x, (uint32_t)lane_xor<2>((int)x));
-  x = max(x, (uint32_t)lane_xor<4>((int)x));
-  x = max(x, (uint32_t)lane_xor<8>((int)x));
-  x = max(x, (uint32_t)lane_xor<16>((int)x));
-  x = max(x, (uint32_t)lane_xor<32>((int)x));
-  return x;
+  x = max(x, dpp_u32<0xB1>(x));
+  x = max(x, dpp_u32<0x4E>(x));
+  x = max(x, dpp_u32<0x141>(x));
+  x = max(x, dpp_u32<0x140>(x));
+  return max(max(rl(x, 0), rl(x, 16)), max(rl(x, 32), rl(x, 48)));
 }
 
 // Wave-wide exact selection threshold over E keys per lane: returns T such
@@ -223,38 +227,6 @@ __device__ __forceinline__ uint64_t wave_select_threshold(const uint64_t (&key)[
   return ((uint64_t)lo << 32) | llo;
 }
 
-// Writes the keys >= T (at most 64 of them) in candidate order to
-// out_s/out_i[0 .. n) and empty entries up to k; `tmp` is 64 words of LDS
-// owned by the wave. Returns n.
-template <int E>
-__device__ __forceinline__ int wave_emit_sorted(const uint64_t (&key)[E], uint64_t T, int k, uint64_t* tmp,
-                                                float* __restrict__ out_s, int* __restrict__ out_i) {
-  const int lane = threadIdx.x & 63;
-  int n = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool sel = key[e] != 0 && key[e] >= T;
-    const unsigned long long m = __ballot(sel);
-    if (sel) {
-      const int p = n + lanes_below(m);
-      if (p < kWave) tmp[p] = key[e];
-    }
-    n += __popcll(m);
-  }
-  if (n > kWave) n = kWave;
-  if (lane < n) {
-    const uint64_t mine = tmp[lane];
-    int r = 0;
-    for (int t = 0; t < n; ++t) r += tmp[t] > mine ? 1 : 0;
-    out_s[r] = key_score(mine);
-    out_i[r] = key_id(mine);
-  } else if (lane < k) {
-    out_s[lane] = neg_inf();
-    out_i[lane] = kSentinelId;
-  }
-  return n;
-}
-
 // ------------------------------------------------ windowed selection
 // A bound T with k <= #{key >= T} <= cap (cap <= 64) over E keys per lane,
 // found by bisection on the score values: only the window has to be hit,
@@ -305,31 +277,65 @@ __device__ __forceinline__ uint64_t wave_window_threshold(const uint64_t (&key)[
 }
 
 // Places the n <= 64 distinct keys tmp[0 .. n) by counting, for each, the
-// keys that precede it; the k best go to out_s/out_i[0 .. k) in candidate
-// order and empty entries fill out[n .. k) when n < k.
-__device__ __forceinline__ void wave_rank_emit(const uint64_t* tmp, int n, int k, float* __restrict__ out_s,
-                                               int* __restrict__ out_i) {
+// keys that precede it; tmp[n .. round_up(n, 8)) must hold zeros (an empty
+// key precedes nothing). The keys are read eight at a time with broadcast
+// LDS reads. The k best go to out_s/out_i[r * stride] (r = 0 .. k-1) in
+// candidate order and empty entries fill ranks n .. k-1 when n < k.
+// Returns the lane's rank (k or more when it holds no winner).
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int wave_rank_emit(const uint64_t* tmp, int n, int k, float* __restrict__ out_s,
+                                              int* __restrict__ out_i, int64_t stride = 1) {
   const int lane = threadIdx.x & 63;
-  if (lane < n) {
-    const uint64_t mine = tmp[lane];
-    int r = 0;
-#pragma unroll 8
-    for (int t = 0; t < n; ++t) r += tmp[t] > mine ? 1 : 0;
-    if (r < k) {
-      out_s[r] = key_score(mine);
-      out_i[r] = key_id(mine);
+  const uint64_t mine = lane < n ? tmp[lane] : 0ull;
+  const u64x2* t2 = reinterpret_cast<const u64x2*>(tmp);
+  int r = 0;
+  for (int t = 0; t < n; t += 16) {
+    // 16 keys (8 broadcast reads) in flight; past n + 8 the reads hit
+    // slots that may hold stale keys, so the second half is counted only
+    // when it lies below round_up(n, 8)
+    u64x2 a[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = t2[t / 2 + q];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r += (a[q].x > mine) + (a[q].y > mine);
+    if (t + 8 < n) {
+#pragma unroll
+      for (int q = 4; q < 8; ++q) r += (a[q].x > mine) + (a[q].y > mine);
     }
-  } else if (lane < k) {
-    out_s[lane] = neg_inf();
-    out_i[lane] = kSentinelId;
   }
+  if (lane < n) {
+    if (r < k) {
+      out_s[r * stride] = key_score(mine);
+      out_i[r * stride] = key_id(mine);
+    }
+  } else {
+    r = k;
+    if (lane < k) {
+      out_s[lane * stride] = neg_inf();
+      out_i[lane * stride] = kSentinelId;
+    }
+  }
+  return r;
+}
+
+// Zeros tmp[n .. round_up(n, 8)) (n <= 64) and makes the wave's LDS writes
+// visible to its own later reads.
+__device__ __forceinline__ void pad_keys(uint64_t* tmp, int n) {
+  const int lane = threadIdx.x & 63;
+  if (lane >= n && lane < ((n + 7) & ~7)) tmp[lane] = 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // The k best of E keys per lane (distinct where non-empty), in candidate
-// order, to out_s/out_i[0 .. k); `tmp` is 64 words of LDS owned by the wave.
+// order, to out_s/out_i[r * stride] (r = 0 .. k-1); `tmp` is 64 words of
+// LDS owned by the wave.
 template <int E>
 __device__ __forceinline__ void wave_topk_emit(const uint64_t (&key)[E], int k, uint64_t* tmp,
-                                               float* __restrict__ out_s, int* __restrict__ out_i) {
+                                               float* __restrict__ out_s, int* __restrict__ out_i,
+                                               int64_t stride = 1) {
   const uint64_t T = wave_window_threshold<E>(key, k, kWave);
   int n = 0;
 #pragma unroll
@@ -343,32 +349,30 @@ __device__ __forceinline__ void wave_topk_emit(const uint64_t (&key)[E], int k, 
     n += __popcll(m);
   }
   n = min(n, kWave);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  wave_rank_emit(tmp, n, k, out_s, out_i);
+  pad_keys(tmp, n);
+  wave_rank_emit(tmp, n, k, out_s, out_i, stride);
 }
 
 // ------------------------------------------------------- sequential merge
 // Wave-wide fallback: folds every list into (s, i), the running best 64 in
 // candidate order, skipping lists whose best entry does not beat the running
-// k-th.
+// k-th. Lists are depth-major: entry j of list p at [j * n + p].
 __device__ __forceinline__ void merge_lists_seq(const float* ps, const int* pi, int n, int k, float& s, int& i) {
   const int lane = threadIdx.x & 63;
   s = neg_inf();
   i = kSentinelId;
   const int j = kWave - 1 - lane;
   for (int p = 0; p < n; ++p) {
-    const float head = ps[(int64_t)p * k];
-    const int head_i = pi[(int64_t)p * k];
+    const float head = ps[p];
+    const int head_i = pi[p];
     const float ks = readlane_f(s, k - 1);
     const int ki = __builtin_amdgcn_readlane(i, k - 1);
     if (!precedes(head, head_i, ks, ki)) continue;
     float os = neg_inf();
     int oi = kSentinelId;
     if (j < k) {
-      os = ps[(int64_t)p * k + j];
-      oi = pi[(int64_t)p * k + j];
+      os = ps[(int64_t)j * n + p];
+      oi = pi[(int64_t)j * n + p];
     }
     merge_reversed(s, i, os, oi);
   }
