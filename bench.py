@@ -135,9 +135,9 @@ def capture(torch, fn, n: int):
 
 
 def event_timed(torch, hip, heads, fn, n: int) -> float:
-    """Mean duration (s) of the selection kernel over n eager calls, timed by
-    events recorded around it. A device-side delay is queued first so the
-    host runs ahead and the events measure the GPU, not the launch rate."""
+    """Mean duration (s) of the score-pass kernel over n eager calls, timed by
+    HIP events attached to its dispatch (start and end of that kernel, on its
+    stream). A device-side delay is queued first so the host runs ahead."""
     evs = [(hip.event(), hip.event()) for _ in range(n)]
     torch.cuda.synchronize()
     torch.cuda._sleep(400_000_000)

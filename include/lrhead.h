@@ -150,11 +150,12 @@ int lrhead_draft(lrhead_t h, const void* H, int64_t B, int k,
 
 /*
  * Profiling aid: hipEvent_t handles (passed as void*) that later calls on
- * this handle record on their stream immediately before and after the
- * vocabulary score/selection kernel (lrhead_candidates, lrhead_draft,
- * fullhead_topk), so a caller can time that kernel with hipEventElapsedTime.
- * Pass NULL, NULL to stop. The events are borrowed; recording them is the
- * only effect.
+ * this handle attach to the dispatch of the vocabulary score pass
+ * (lrhead_candidates, lrhead_draft, fullhead_topk; for row batches its main
+ * GEMM pass): the first records the kernel's start, the second its end, so
+ * hipEventElapsedTime gives that kernel's own duration. Pass NULL, NULL to
+ * stop. The events are borrowed; recording them is the only effect. Calls
+ * with events set must not be captured into a HIP graph.
  */
 int lrhead_set_stage_events(lrhead_t h, void* before, void* after);
 

@@ -470,7 +470,7 @@ hipError_t allow_lds() {
 template <class C>
 hipError_t run_gemm(int mode, const uint16_t* M, const uint16_t* X, int64_t V, int K, int64_t B, int nvb,
                     int stride, float* tmax, int ns_tiles, const float* theta, float* S, int64_t ldS,
-                    uint32_t* mask, int NW, hipStream_t stream) {
+                    uint32_t* mask, int NW, hipStream_t stream, Timing t = {}) {
   const int64_t NT = (B + C::BN - 1) / C::BN;
   const int64_t nvb_pad = (nvb + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)(nvb_pad * NT));
@@ -479,15 +479,14 @@ hipError_t run_gemm(int mode, const uint16_t* M, const uint16_t* X, int64_t V, i
     hipLaunchKernelGGL((gemm_sel_kernel<C, kModeMax>), grid, dim3(kGemmThreads), lds, stream, M, X, V, K, B, nvb,
                        stride, tmax, ns_tiles, theta, S, ldS, mask, NW);
   else
-    hipLaunchKernelGGL((gemm_sel_kernel<C, kModeFilter>), grid, dim3(kGemmThreads), lds, stream, M, X, V, K, B,
-                       nvb, stride, tmax, ns_tiles, theta, S, ldS, mask, NW);
+    LRH_LAUNCH(t, (gemm_sel_kernel<C, kModeFilter>), grid, dim3(kGemmThreads), lds, stream, M, X, V, K, B, nvb,
+               stride, tmax, ns_tiles, theta, S, ldS, mask, NW);
   return hipGetLastError();
 }
 
 template <class C>
 hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, int64_t V, int K, int64_t B, int k,
-                    const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream, hipEvent_t ev_before,
-                    hipEvent_t ev_after) {
+                    const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream, Timing t) {
   hipError_t e = run_gemm<C>(kModeMax, M, X, V, K, B, p.ns, p.stride, w.tmax, p.ns_tiles, nullptr, nullptr, 0,
                              nullptr, 0, stream);
   if (e != hipSuccess) return e;
@@ -495,11 +494,9 @@ hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, in
   hipLaunchKernelGGL(theta_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, stream, w.tmax, p.ns_tiles, B, k,
                      cap, w.theta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev_before && (e = hipEventRecord(ev_before, stream)) != hipSuccess) return e;
   e = run_gemm<C>(kModeFilter, M, X, V, K, B, (int)p.nvb, 1, nullptr, 0, w.theta, w.S, p.ldS, w.mask, p.NW,
-                  stream);
+                  stream, t);
   if (e != hipSuccess) return e;
-  if (ev_after && (e = hipEventRecord(ev_after, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(collect_kernel<C::TM>, dim3((unsigned)B), dim3(kGemmThreads), 0, stream, w.mask, p.NW, w.S,
                      p.ldS, B, k, idx, score);
   return hipGetLastError();
@@ -554,13 +551,12 @@ BatchScratch batch_scratch(void* base, int64_t V, int64_t B_max) {
 }
 
 hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, int64_t B, int k,
-                               const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream,
-                               hipEvent_t ev_before, hipEvent_t ev_after) {
+                               const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream, Timing t) {
   const BatchPlan p = plan_batch(V, B, k);
   const uint16_t* m = static_cast<const uint16_t*>(M);
   const uint16_t* x = static_cast<const uint16_t*>(X);
-  if (B <= 64) return run_pass<CfgNarrow>(p, m, x, V, K, B, k, w, idx, score, stream, ev_before, ev_after);
-  return run_pass<CfgWide>(p, m, x, V, K, B, k, w, idx, score, stream, ev_before, ev_after);
+  if (B <= 64) return run_pass<CfgNarrow>(p, m, x, V, K, B, k, w, idx, score, stream, t);
+  return run_pass<CfgWide>(p, m, x, V, K, B, k, w, idx, score, stream, t);
 }
 
 }  // namespace lrh

@@ -264,10 +264,10 @@ hipError_t launch_down(int dtype, const void* Q, const void* H, int r, int d, in
 }
 
 hipError_t launch_select(int dtype, const void* M, const void* X, int64_t V, int K, int64_t B, int k,
-                         int n_vsplit, float* part_s, int* part_i, hipStream_t stream) {
+                         int n_vsplit, float* part_s, int* part_i, hipStream_t stream, Timing t) {
   dim3 grid(n_vsplit, (unsigned)((B + kTile - 1) / kTile));
-  LRH_DISPATCH(dtype, hipLaunchKernelGGL(select_mfma_kernel<T>, grid, dim3(256), 0, stream, (const T*)M,
-                                         (const T*)X, V, K, B, k, n_vsplit, part_s, part_i));
+  LRH_DISPATCH(dtype, LRH_LAUNCH(t, select_mfma_kernel<T>, grid, dim3(256), 0, stream, (const T*)M, (const T*)X, V,
+                                 K, B, k, n_vsplit, part_s, part_i));
   return hipGetLastError();
 }
 

@@ -307,44 +307,44 @@ hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t
 
 template <int K>
 static hipError_t launch_short_k(const void* M, const void* X, int64_t V, int64_t B, int k, float* ps, int* pi,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, Timing t) {
   const int nblk = small_blocks(V);
   dim3 grid(nblk);
   const int64_t rows = (V + nblk - 1) / nblk;   // most rows of one block
   if (rows <= 4 * kWave) {
-    LRH_NB_DISPATCH(B, hipLaunchKernelGGL((select_short_kernel<K, NB, 4>), grid, dim3(kSmallThreads), 0, stream,
-                                          (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
+    LRH_NB_DISPATCH(B, LRH_LAUNCH(t, (select_short_kernel<K, NB, 4>), grid, dim3(kSmallThreads), 0, stream,
+                                  (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
   } else if (rows <= 5 * kWave) {
-    LRH_NB_DISPATCH(B, hipLaunchKernelGGL((select_short_kernel<K, NB, 5>), grid, dim3(kSmallThreads), 0, stream,
-                                          (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
+    LRH_NB_DISPATCH(B, LRH_LAUNCH(t, (select_short_kernel<K, NB, 5>), grid, dim3(kSmallThreads), 0, stream,
+                                  (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
   } else {
-    LRH_NB_DISPATCH(B, hipLaunchKernelGGL((select_short_kernel<K, NB, 8>), grid, dim3(kSmallThreads), 0, stream,
-                                          (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
+    LRH_NB_DISPATCH(B, LRH_LAUNCH(t, (select_short_kernel<K, NB, 8>), grid, dim3(kSmallThreads), 0, stream,
+                                  (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
   }
   return hipGetLastError();
 }
 
 hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* ps,
-                               int* pi, hipStream_t stream) {
+                               int* pi, hipStream_t stream, Timing t) {
   switch (K) {
-    case 8: return launch_short_k<8>(M, X, V, B, k, ps, pi, stream);
-    case 16: return launch_short_k<16>(M, X, V, B, k, ps, pi, stream);
-    case 32: return launch_short_k<32>(M, X, V, B, k, ps, pi, stream);
-    case 64: return launch_short_k<64>(M, X, V, B, k, ps, pi, stream);
-    case 128: return launch_short_k<128>(M, X, V, B, k, ps, pi, stream);
-    case 256: return launch_short_k<256>(M, X, V, B, k, ps, pi, stream);
-    case 512: return launch_short_k<512>(M, X, V, B, k, ps, pi, stream);
+    case 8: return launch_short_k<8>(M, X, V, B, k, ps, pi, stream, t);
+    case 16: return launch_short_k<16>(M, X, V, B, k, ps, pi, stream, t);
+    case 32: return launch_short_k<32>(M, X, V, B, k, ps, pi, stream, t);
+    case 64: return launch_short_k<64>(M, X, V, B, k, ps, pi, stream, t);
+    case 128: return launch_short_k<128>(M, X, V, B, k, ps, pi, stream, t);
+    case 256: return launch_short_k<256>(M, X, V, B, k, ps, pi, stream, t);
+    case 512: return launch_short_k<512>(M, X, V, B, k, ps, pi, stream, t);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* ps,
-                              int* pi, hipStream_t stream) {
+                              int* pi, hipStream_t stream, Timing t) {
   dim3 grid(small_blocks(V));
   const int nl = row_loads(K);
-  LRH_NB_DISPATCH(B, LRH_NL_DISPATCH(nl, hipLaunchKernelGGL((select_long_kernel<NB, NL>), grid,
-                                                               dim3(kSmallThreads), 0, stream, (const uint16_t*)M,
-                                                               (const uint16_t*)X, V, K, (int)B, k, ps, pi)));
+  LRH_NB_DISPATCH(B, LRH_NL_DISPATCH(nl, LRH_LAUNCH(t, (select_long_kernel<NB, NL>), grid, dim3(kSmallThreads), 0,
+                                                    stream, (const uint16_t*)M, (const uint16_t*)X, V, K, (int)B, k,
+                                                    ps, pi)));
   return hipGetLastError();
 }
 

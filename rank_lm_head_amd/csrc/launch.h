@@ -2,10 +2,27 @@
 // library; the public interface is include/lrhead.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace lrh {
+
+// Optional events attached to one kernel's dispatch: they record its start
+// and end (the profiling hook of the score pass).
+struct Timing {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+#define LRH_LAUNCH(timing, kernel, grid, block, shm, stream, ...)                                    \
+  do {                                                                                           \
+    if ((timing).start)                                                                          \
+      hipExtLaunchKernelGGL(kernel, grid, block, shm, stream, (timing).start, (timing).stop, 0,  \
+                            __VA_ARGS__);                                                        \
+    else                                                                                         \
+      hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);                         \
+  } while (0)
 
 // Draft-row counts up to this use the streaming (vector ALU) kernels of
 // kernels_small.hip; larger batches use the matrix-core kernels.
@@ -23,9 +40,9 @@ hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t
 // Streaming score pass: per block, the k best of its slice for each row,
 // written depth-major: entry j of block x's list at part_[row][j][x].
 hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
-                               int* part_i, hipStream_t stream);
+                               int* part_i, hipStream_t stream, Timing t = {});
 hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
-                              int* part_i, hipStream_t stream);
+                              int* part_i, hipStream_t stream, Timing t = {});
 
 // ------------------------------------------------------ kernels_mfma.hip
 // Vocabulary slices of the matrix-core selection pass for B rows over V
@@ -39,7 +56,7 @@ hipError_t launch_down(int dtype, const void* Q, const void* H, int r, int d, in
 // Per-slice candidate lists of "M . x" for B rows: M is V x K (P or W),
 // X is B x K (z or h). Writes part_s / part_i: [B][k][n_vsplit].
 hipError_t launch_select(int dtype, const void* M, const void* X, int64_t V, int K, int64_t B,
-                         int k, int n_vsplit, float* part_s, int* part_i, hipStream_t stream);
+                         int k, int n_vsplit, float* part_s, int* part_i, hipStream_t stream, Timing t = {});
 
 // Dense logits[b, v] = W[v, :] . h_b for all V (test aid).
 hipError_t launch_dense(int dtype, const void* W, const void* H, int64_t V, int d, int64_t B,
@@ -72,11 +89,11 @@ BatchScratch batch_scratch(void* base, int64_t V, int64_t B_max);
 hipError_t batch_init();
 
 // The k best of every row of X . M^T (M is V x K, X is B x K, bf16) in
-// candidate order to idx / score (score may be NULL). Events, when given,
-// are recorded around the main GEMM pass.
+// candidate order to idx / score (score may be NULL). `t` times the main
+// GEMM pass.
 hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, int64_t B, int k,
                                const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream,
-                               hipEvent_t ev_before, hipEvent_t ev_after);
+                               Timing t = {});
 
 // ----------------------------------------------------- kernels_merge.hip
 // Merges n sorted lists of k per row (part_[row][entry][list], n <= 512) into

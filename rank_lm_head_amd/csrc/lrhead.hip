@@ -30,8 +30,8 @@ struct lrhead_s {
   int* part_i;
   bool batch;       // bf16 with B_max > 4: the GEMM path's scratch exists
   lrh::BatchScratch bw;
-  hipEvent_t ev_before;  // optional events around the selection kernel
-  hipEvent_t ev_after;
+  hipEvent_t ev_before;  // optional events attached to the score pass: its start
+  hipEvent_t ev_after;   // and its end
 };
 
 namespace {
@@ -136,11 +136,8 @@ int check_out(const void* p, const char* name, bool required) {
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
 
-int record(hipEvent_t ev, hipStream_t s) {
-  if (!ev) return LRHEAD_OK;
-  const hipError_t e = hipEventRecord(ev, s);
-  return e == hipSuccess ? LRHEAD_OK : hip_fail(e, "hipEventRecord");
-}
+// The caller's profiling events, attached to the score pass's dispatch.
+lrh::Timing timing(const lrhead_s* h) { return lrh::Timing{h->ev_before, h->ev_after}; }
 
 // Down-projection, score pass with per-slice selection, and the merge of
 // the slice lists; with `logits`, the merge also rescores the winners.
@@ -148,8 +145,7 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
                  hipStream_t s) {
   if (lrh::batch_path(h->dtype, B)) {
     LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
-    LRH_HIP(lrh::launch_batch_select(h->P, h->z, h->V, (int)h->r, B, k, h->bw, idx, score, s, h->ev_before,
-                                     h->ev_after),
+    LRH_HIP(lrh::launch_batch_select(h->P, h->z, h->V, (int)h->r, B, k, h->bw, idx, score, s, timing(h)),
             "score/selection launch");
     if (logits)
       LRH_HIP(lrh::launch_rescore(h->dtype, h->W, H, idx, B, k, h->V, (int)h->d, logits, s), "rescore launch");
@@ -158,18 +154,15 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   int n_lists;
   if (lrh::small_path(h->dtype, B, h->r, h->V)) {
     LRH_HIP(lrh::launch_down_small(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
-    LRH_TRY(record(h->ev_before, s));
-    LRH_HIP(lrh::launch_select_small(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, s),
+    LRH_HIP(lrh::launch_select_small(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, s, timing(h)),
             "score/selection launch");
-    LRH_TRY(record(h->ev_after, s));
     n_lists = lrh::small_blocks(h->V);
   } else {
     LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
     n_lists = lrh::plan_vsplit(B, h->V);
-    LRH_TRY(record(h->ev_before, s));
-    LRH_HIP(lrh::launch_select(h->dtype, h->P, h->z, h->V, (int)h->r, B, k, n_lists, h->part_s, h->part_i, s),
+    LRH_HIP(lrh::launch_select(h->dtype, h->P, h->z, h->V, (int)h->r, B, k, n_lists, h->part_s, h->part_i, s,
+                               timing(h)),
             "score/selection launch");
-    LRH_TRY(record(h->ev_after, s));
   }
   LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, h->V, B, k, h->W, H, (int)h->d, idx, score,
                             logits, s),
@@ -269,24 +262,20 @@ int fullhead_topk(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, flo
   if (B == 0) return LRHEAD_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (lrh::batch_path(h->dtype, B)) {
-    LRH_HIP(lrh::launch_batch_select(h->W, H, h->V, (int)h->d, B, k, h->bw, idx, logits, s, h->ev_before,
-                                     h->ev_after),
+    LRH_HIP(lrh::launch_batch_select(h->W, H, h->V, (int)h->d, B, k, h->bw, idx, logits, s, timing(h)),
             "full-head selection launch");
     return LRHEAD_OK;
   }
   int n_lists;
   if (lrh::small_long_path(h->dtype, B, h->d, h->V)) {
     n_lists = lrh::small_blocks(h->V);
-    LRH_TRY(record(h->ev_before, s));
-    LRH_HIP(lrh::launch_select_long(h->W, H, h->V, (int)h->d, B, k, h->part_s, h->part_i, s),
+    LRH_HIP(lrh::launch_select_long(h->W, H, h->V, (int)h->d, B, k, h->part_s, h->part_i, s, timing(h)),
             "full-head selection launch");
-    LRH_TRY(record(h->ev_after, s));
   } else {
     n_lists = lrh::plan_vsplit(B, h->V);
-    LRH_TRY(record(h->ev_before, s));
-    LRH_HIP(lrh::launch_select(h->dtype, h->W, H, h->V, (int)h->d, B, k, n_lists, h->part_s, h->part_i, s),
+    LRH_HIP(lrh::launch_select(h->dtype, h->W, H, h->V, (int)h->d, B, k, n_lists, h->part_s, h->part_i, s,
+                               timing(h)),
             "full-head selection launch");
-    LRH_TRY(record(h->ev_after, s));
   }
   LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, h->V, B, k, nullptr, nullptr, (int)h->d, idx,
                             logits, nullptr, s),

@@ -134,7 +134,7 @@ class Head:
         return idx, score, logits
 
     def set_stage_events(self, before, after) -> None:
-        """Record two hipEvent_t handles (ints or None) around the selection kernel."""
+        """Attach two hipEvent_t handles (ints or None) to the score pass's dispatch: its start and end."""
         _lib.check(self.lib.lrhead_set_stage_events(self._h, before, after), "lrhead_set_stage_events")
 
     def close(self) -> None:
