@@ -10,6 +10,6 @@ from .lowrank_head import (  # noqa: F401
     full_head,
 )
 from .compare import (  # noqa: F401
-    check_candidates, check_logits, check_scores, band_counts, LOGIT_RTOL,
-    SCORE_TOL,
+    check_candidates, check_logits, check_scores, band_counts, ulp_bf16,
+    z_step_allowance, LOGIT_RTOL, SCORE_TOL,
 )

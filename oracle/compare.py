@@ -19,8 +19,15 @@ Order:  consecutive device ids follow the oracle's order (higher score, then
 Logits: |got - exact| <= rtol * max(|exact|, 1e-2 * max_j |exact_j|), with
         rtol = 2e-3 for bf16 and 1e-5 for fp32, exact = the oracle's
         full-rank logit at the *device's* id.
-Scores: (diagnostic) |got - s[id]| <= f * max_v |s[v]|, f = 1e-4 (bf16) or
-        1e-6 (fp32).
+Scores: (diagnostic) |got - s[id]| <= f * max_v |s[v]| + a_id, f = 1e-4
+        (bf16) or 1e-6 (fp32), where a_id allows one bf16 step of one
+        component of z: the stored z is the fp32 accumulator rounded to
+        bf16, and when the exact z_j lies within the accumulator's own
+        rounding error of a bf16 midpoint, an accumulation order other than
+        the oracle's exact-then-round may land on the neighbouring bf16
+        value. a_id = max_j |P[id, j]| * ulp_bf16(z_j) (0 for fp32 heads,
+        whose z is not rounded to bf16). Such a step moves scores by far
+        less than tau, so the index rules are unaffected.
 """
 from __future__ import annotations
 
@@ -82,11 +89,28 @@ def check_logits(got: np.ndarray, exact: np.ndarray, dtype: str) -> list[str]:
     return []
 
 
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values (8 significant bits) at |x|; 0 at x == 0."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(x > 0, x, 1.0)))
+    return np.where(x > 0, 2.0 ** (e - 7), 0.0)
+
+
+def z_step_allowance(P_rows: np.ndarray, z_row: np.ndarray, dtype: str) -> np.ndarray:
+    """a_id of the score rule for the given rows of P (float64) and the
+    oracle's stored z of the draft row: max_j |P[id, j]| * ulp_bf16(z_j)."""
+    if dtype != "bf16":
+        return np.zeros(P_rows.shape[0])
+    return np.max(np.abs(P_rows) * ulp_bf16(z_row)[None, :], axis=1)
+
+
 def check_scores(got: np.ndarray, s_at: np.ndarray, s_row_absmax: float,
-                 dtype: str) -> list[str]:
-    """Score diagnostic for one row."""
+                 dtype: str, allowance: np.ndarray | None = None) -> list[str]:
+    """Score diagnostic for one row (`allowance` = a_id per entry)."""
     got = np.asarray(got, dtype=np.float64).ravel()
     tol = SCORE_TOL[dtype] * s_row_absmax
+    if allowance is not None:
+        tol = tol + np.asarray(allowance, dtype=np.float64).ravel()
     bad = np.nonzero(~(np.abs(got - s_at) <= tol))[0]
     if bad.size:
         j = bad[0]

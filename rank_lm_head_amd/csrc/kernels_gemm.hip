@@ -58,7 +58,7 @@ struct GemmCfg {
   static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the loaders");
 };
 
-enum { kModeMax = 0, kModeFilter = 1 };
+enum { kModeMax = 0, kModeFilter = 1, kModeStore = 2 };
 
 __device__ __forceinline__ int swz(int row, int c) { return row * kRowChunks + (c ^ (row & 7)); }
 
@@ -157,9 +157,15 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
 
   const int NT = (int)((B + C::BN - 1) / C::BN);
   const int L = blockIdx.x;
-  const int xcd = L % kXcds, j = L / kXcds;
-  const int vb_local = (j / NT) * kXcds + xcd;
-  const int nt = j % NT;
+  int vb_local, nt;
+  if (nvb >= kXcds) {
+    const int xcd = L % kXcds, j = L / kXcds;
+    vb_local = (j / NT) * kXcds + xcd;
+    nt = j % NT;
+  } else {   // too few vocabulary blocks to spread over the XCDs
+    vb_local = L / NT;
+    nt = L % NT;
+  }
   if (vb_local >= nvb) return;
   const int vb = vb_local * stride;
   const int64_t m0 = (int64_t)vb * C::BM;
@@ -241,6 +247,28 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
           if (vrow + i * 16 + q < V) m = fmaxf(m, acc[i][jn][q]);
         m = fmax_lanes(m);
         if (g == 0 && n < B) aux_f[n * ns_tiles + vb_local * (C::BM / 16) + wm * C::FM + i] = m;
+      }
+    }
+  } else if constexpr (MODE == kModeStore) {
+    // the product itself, rounded to bf16: Z row n at S + n * ldS (bf16)
+    uint16_t* Z = reinterpret_cast<uint16_t*>(S);
+#pragma unroll
+    for (int jn = 0; jn < C::FN; ++jn) {
+      const int64_t n = n0 + wn * C::TN + jn * 16 + col;
+      if (n >= B) continue;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        const int64_t m = vrow + i * 16;
+        uint16_t* z = Z + n * ldS + m;
+        if (m + 4 <= V) {
+          const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][jn][0]) | ((uint32_t)f32_to_bf16(acc[i][jn][1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(acc[i][jn][2]) | ((uint32_t)f32_to_bf16(acc[i][jn][3]) << 16);
+          *reinterpret_cast<uint2*>(z) = uint2{lo, hi};
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (m + q < V) z[q] = f32_to_bf16(acc[i][jn][q]);
+        }
       }
     }
   } else {
@@ -326,108 +354,128 @@ __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ tm
 }
 
 // ----------------------------------------------------------------- collect
-constexpr int kCollectCap = 4096;                       // flagged scores per round
-constexpr int kCollectE = kCollectCap / kGemmThreads;   // keys per lane per wave
+// One wave per row (four rows per block). The row's mask words are read in
+// chunks of 16-byte loads; each lane counts its flags, and a prefix over
+// the lanes (from the bit planes of the counts) gives every flag a slot.
+// Flagged vocabulary ids go to LDS, then their scores are fetched in
+// batches (independent loads) and ranked. A row with more than kColCap
+// flags (ties) is taken in rounds of kColCap slots, each round's best k
+// merged into a running list.
+constexpr int kColCap = 1024;
+constexpr int kColE = kColCap / kWave;
 
-struct CollectSmem {
-  uint64_t buf[kCollectCap];
-  uint64_t tmp[4][kWave];
-  float ws[5][kWave];       // lists 0..3: the waves' best; 4: running best
-  int wi[5][kWave];
-  int wave_tot[4];
-  int total;
+struct CollectWave {
+  uint64_t key[kColCap];
+  int vid[kColCap];
+  uint64_t tmp[kWave];
+  float ls[2][kWave];   // 0: this round's best, 1: running best
+  int li[2][kWave];
 };
 
-// Exclusive prefix over the block of per-thread counts; returns the
-// thread's offset and writes the total to `total`.
-__device__ __forceinline__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int incl = x;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
-  if (lane == kWave - 1) wave_tot[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) before += wave_tot[w];
-    all += wave_tot[w];
-  }
-  if (threadIdx.x == 0) *total = all;
-  __syncthreads();
-  return before + incl - x;
-}
-
-// One block per row: the k best flagged scores of the row, in candidate
-// order, to idx / score (sentinel ids when fewer than k are flagged).
 template <int TM>
 __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* __restrict__ mask, int NW,
                                                                 const float* __restrict__ S, int64_t ldS, int64_t B,
                                                                 int k, int32_t* __restrict__ idx,
                                                                 float* __restrict__ score) {
-  __shared__ CollectSmem m;
+  __shared__ CollectWave cw[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = blockIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= B) return;
+  CollectWave& m = cw[wave];
   const uint32_t* mw = mask + row * NW;
   const float* sr = S + row * ldS;
 
+  // the lane's words, chunk c: w = 4 * (lane + 64 * (c * T4 + t)) + 0..3
+  constexpr int T4 = 8;
+  const int nq = (NW + 3) / 4;
+  const int nchunk = (nq + kWave * T4 - 1) / (kWave * T4);
+  auto load_chunk = [&](int c, u32x4 (&wd)[T4]) {
+#pragma unroll
+    for (int t = 0; t < T4; ++t) {
+      const int q = lane + kWave * (c * T4 + t);
+      wd[t] = *reinterpret_cast<const u32x4*>(mw + 4 * min(q, nq - 1));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (q >= nq || 4 * q + e >= NW) wd[t][e] = 0u;
+    }
+  };
   int cnt = 0;
-  for (int w = threadIdx.x; w < NW; w += kGemmThreads) cnt += __popc(mw[w]);
-  const int off = block_exclusive_scan(cnt, m.wave_tot, &m.total);
-  const int C = m.total;
-  if (threadIdx.x < kWave) {
-    m.ws[4][threadIdx.x] = neg_inf();
-    m.wi[4][threadIdx.x] = kSentinelId;
+  for (int c = 0; c < nchunk; ++c) {
+    u32x4 wd[T4];
+    load_chunk(c, wd);
+#pragma unroll
+    for (int t = 0; t < T4; ++t) cnt += __popc(wd[t][0]) + __popc(wd[t][1]) + __popc(wd[t][2]) + __popc(wd[t][3]);
   }
-  for (int base = 0; base < C; base += kCollectCap) {
-    int pos = off;
-    for (int w = threadIdx.x; w < NW; w += kGemmThreads) {
-      uint32_t bits = mw[w];
-      const int64_t slice = w >> 2, gq = w & 3;
-      while (bits) {
-        const int b = __builtin_ctz(bits);
-        bits &= bits - 1;
-        if (pos >= base && pos < base + kCollectCap) {
-          const int64_t v = slice * TM + (b >> 2) * 16 + 4 * gq + (b & 3);
-          m.buf[pos - base] = cand_key(sr[v], (int)v);
-        }
-        ++pos;
-      }
-    }
-    __syncthreads();
-    const int n = min(kCollectCap, C - base);
-    {
-      uint64_t key[kCollectE];
+  int before = 0, C = 0;
 #pragma unroll
-      for (int e = 0; e < kCollectE; ++e) {
-        const int jj = wave * (kCollectCap / 4) + e * kWave + lane;
-        key[e] = jj < n ? m.buf[jj] : 0ull;
-      }
-      wave_topk_emit<kCollectE>(key, k, m.tmp[wave], m.ws[wave], m.wi[wave]);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      uint64_t key[5];
+  for (int bit = 0; bit < 20; ++bit) {   // counts below 2^20
+    const unsigned long long plane = __ballot((cnt >> bit) & 1);
+    before += lanes_below(plane) << bit;
+    C += __popcll(plane) << bit;
+  }
+  if (lane < kWave) {
+    m.ls[1][lane] = neg_inf();
+    m.li[1][lane] = kSentinelId;
+  }
+  for (int base = 0; base < max(C, 1); base += kColCap) {
+    const int n = min(kColCap, C - base);
+    // ids of the slots [base, base + n)
+    int pos = before;
+    for (int c = 0; c < nchunk; ++c) {
+      u32x4 wd[T4];
+      load_chunk(c, wd);
 #pragma unroll
-      for (int e = 0; e < 5; ++e) {
-        const int jj = e * kWave + lane;
-        const int list = jj / k, p = jj - list * k;
-        key[e] = 0ull;
-        if (list < 5) {
-          const int id = m.wi[list][p];
-          if (id != kSentinelId) key[e] = cand_key(m.ws[list][p], id);
+      for (int t = 0; t < T4; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t bits = wd[t][e];
+          const int w = 4 * (lane + kWave * (c * T4 + t)) + e;
+          const int64_t slice = w >> 2, gq = w & 3;
+          while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1;
+            if (pos >= base && pos < base + kColCap)
+              m.vid[pos - base] = (int)(slice * TM + (b >> 2) * 16 + 4 * gq + (b & 3));
+            ++pos;
+          }
         }
       }
-      wave_topk_emit<5>(key, k, m.tmp[0], m.ws[4], m.wi[4]);
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // their scores, 8 independent loads per lane at a time
+    uint64_t key[kColE];
+#pragma unroll
+    for (int e = 0; e < kColE; ++e) {
+      const int j = e * kWave + lane;
+      const int v = j < n ? m.vid[j] : 0;
+      const float x = sr[v];
+      key[e] = j < n ? cand_key(x, v) : 0ull;
+    }
+    if (C <= kColCap) {
+      // one round: straight to the output
+      wave_topk_emit<kColE>(key, k, m.tmp, m.ls[1], m.li[1]);
+    } else {
+      wave_topk_emit<kColE>(key, k, m.tmp, m.ls[0], m.li[0]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint64_t k2[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int id = lane < k ? m.li[e][lane] : kSentinelId;
+        k2[e] = id != kSentinelId ? cand_key(m.ls[e][lane], id) : 0ull;
+      }
+      wave_topk_emit<2>(k2, k, m.tmp, m.ls[1], m.li[1]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  if (threadIdx.x < k) {
-    idx[row * k + threadIdx.x] = m.wi[4][threadIdx.x];
-    if (score) score[row * k + threadIdx.x] = m.ws[4][threadIdx.x];
+  if (lane < k) {
+    idx[row * k + lane] = m.li[1][lane];
+    if (score) score[row * k + lane] = m.ls[1][lane];
   }
 }
 
@@ -437,6 +485,7 @@ namespace {
 
 using CfgWide = GemmCfg<256, 128, 2, 2>;    // B > 64
 using CfgNarrow = GemmCfg<256, 64, 4, 1>;   // B <= 64
+using CfgDown = GemmCfg<64, 64, 2, 2>;      // z = Q . h for many rows (r is small)
 
 constexpr int kGemmBM = 256;
 
@@ -460,11 +509,13 @@ size_t gemm_lds_bytes(int K = 1 << 30) {
 
 template <class C>
 hipError_t allow_lds() {
-  hipError_t e = hipFuncSetAttribute((const void*)gemm_sel_kernel<C, kModeMax>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes<C>());
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)gemm_sel_kernel<C, kModeFilter>,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes<C>());
+  for (const void* f : {(const void*)gemm_sel_kernel<C, kModeMax>, (const void*)gemm_sel_kernel<C, kModeFilter>,
+                        (const void*)gemm_sel_kernel<C, kModeStore>}) {
+    const hipError_t e =
+        hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes<C>());
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <class C>
@@ -472,11 +523,14 @@ hipError_t run_gemm(int mode, const uint16_t* M, const uint16_t* X, int64_t V, i
                     int stride, float* tmax, int ns_tiles, const float* theta, float* S, int64_t ldS,
                     uint32_t* mask, int NW, hipStream_t stream, Timing t = {}) {
   const int64_t NT = (B + C::BN - 1) / C::BN;
-  const int64_t nvb_pad = (nvb + kXcds - 1) / kXcds * kXcds;
+  const int64_t nvb_pad = nvb >= kXcds ? (nvb + kXcds - 1) / kXcds * kXcds : nvb;
   const dim3 grid((unsigned)(nvb_pad * NT));
   const size_t lds = gemm_lds_bytes<C>(K);
   if (mode == kModeMax)
     hipLaunchKernelGGL((gemm_sel_kernel<C, kModeMax>), grid, dim3(kGemmThreads), lds, stream, M, X, V, K, B, nvb,
+                       stride, tmax, ns_tiles, theta, S, ldS, mask, NW);
+  else if (mode == kModeStore)
+    hipLaunchKernelGGL((gemm_sel_kernel<C, kModeStore>), grid, dim3(kGemmThreads), lds, stream, M, X, V, K, B, nvb,
                        stride, tmax, ns_tiles, theta, S, ldS, mask, NW);
   else
     LRH_LAUNCH(t, (gemm_sel_kernel<C, kModeFilter>), grid, dim3(kGemmThreads), lds, stream, M, X, V, K, B, nvb,
@@ -497,8 +551,8 @@ hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, in
   e = run_gemm<C>(kModeFilter, M, X, V, K, B, (int)p.nvb, 1, nullptr, 0, w.theta, w.S, p.ldS, w.mask, p.NW,
                   stream, t);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(collect_kernel<C::TM>, dim3((unsigned)B), dim3(kGemmThreads), 0, stream, w.mask, p.NW, w.S,
-                     p.ldS, B, k, idx, score);
+  hipLaunchKernelGGL(collect_kernel<C::TM>, dim3((unsigned)((B + 3) / 4)), dim3(kGemmThreads), 0, stream, w.mask,
+                     p.NW, w.S, p.ldS, B, k, idx, score);
   return hipGetLastError();
 }
 
@@ -509,7 +563,14 @@ bool batch_path(int dtype, int64_t B) { return dtype == 0 && B > kSmallB; }
 hipError_t batch_init() {
   hipError_t e = allow_lds<CfgWide>();
   if (e == hipSuccess) e = allow_lds<CfgNarrow>();
+  if (e == hipSuccess) e = allow_lds<CfgDown>();
   return e;
+}
+
+hipError_t launch_down_gemm(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream) {
+  const int nvb = (r + CfgDown::BM - 1) / CfgDown::BM;
+  return run_gemm<CfgDown>(kModeStore, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(H), r, d, B,
+                           nvb, 1, nullptr, 0, nullptr, static_cast<float*>(Z), r, nullptr, 0, stream);
 }
 
 BatchPlan plan_batch(int64_t V, int64_t B, int k) {

@@ -87,6 +87,8 @@ size_t batch_scratch_bytes(int64_t V, int64_t B_max);
 BatchScratch batch_scratch(void* base, int64_t V, int64_t B_max);
 // Lets the GEMM kernels use more than 64 KiB of LDS (call once per device).
 hipError_t batch_init();
+// z = round_bf16(Q . h) for B rows on the GEMM kernel (bf16 only).
+hipError_t launch_down_gemm(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream);
 
 // The k best of every row of X . M^T (M is V x K, X is B x K, bf16) in
 // candidate order to idx / score (score may be NULL). `t` times the main

@@ -37,6 +37,7 @@ struct lrhead_s {
 namespace {
 
 constexpr uint32_t kMagic = 0x4c524844u;  // "LRHD"
+constexpr int64_t kDownGemmRows = 256;     // rows from which z = Q . h runs on the GEMM kernel
 constexpr int64_t kBMaxLimit = int64_t(1) << 20;
 
 thread_local char g_err[512] = "";
@@ -144,7 +145,11 @@ lrh::Timing timing(const lrhead_s* h) { return lrh::Timing{h->ev_before, h->ev_a
 int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, float* score, float* logits,
                  hipStream_t s) {
   if (lrh::batch_path(h->dtype, B)) {
-    LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
+    // many rows: the down-projection is a GEMM worth the pipelined kernel
+    if (B >= kDownGemmRows)
+      LRH_HIP(lrh::launch_down_gemm(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
+    else
+      LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
     LRH_HIP(lrh::launch_batch_select(h->P, h->z, h->V, (int)h->r, B, k, h->bw, idx, score, s, timing(h)),
             "score/selection launch");
     if (logits)

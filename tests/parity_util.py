@@ -27,7 +27,9 @@ def check_lowrank(inp: dict, k: int, idx, score, logits, rows=None) -> tuple[lis
         s = ref["s"][i]
         e = oracle.check_candidates(idx[b], s, ref["idx"][i], ref["tau"][i], ref["gap"][i], ref["s_k"][i])
         if score is not None:
-            e += oracle.check_scores(score[b], s[idx[b]], float(np.max(np.abs(s))), dt)
+            ids = np.clip(idx[b].astype(np.int64), 0, inp["P"].shape[0] - 1)
+            allow = oracle.z_step_allowance(oracle.to_f64(inp["P"][ids], dt), ref["z"][i], dt)
+            e += oracle.check_scores(score[b], s[idx[b]], float(np.max(np.abs(s))), dt, allow)
         if logits is not None:
             exact = oracle.exact_logits(inp["W"], h64, np.full(k, i), idx[b].astype(np.int64), dt)
             e += oracle.check_logits(logits[b], exact, dt)

@@ -122,6 +122,8 @@ def test_streaming_path_shapes(V, d, r, B, k):
     (6000, 384, 256, 64, 64),    # narrow batch tile exactly full, k = 64
     (12345, 200, 72, 65, 10),    # one row past the narrow tile; K = 64 + 8
     (257, 64, 16, 9, 9),         # two vocabulary blocks, the second holding one row
+    (3000, 200, 72, 300, 16),    # z on the GEMM kernel: r = 64 + 8, d = 3 * 64 + 8, ragged row tile
+    (5000, 512, 256, 512, 64),   # z on the GEMM kernel, full tiles
 ])
 def test_batch_path_shapes(V, d, r, B, k):
     inp = gen.make_custom(V, d, r, B, "bf16", seed=V + B)

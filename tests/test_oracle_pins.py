@@ -336,6 +336,38 @@ def test_comparison_rule_catches_planted_mistakes():
     assert compare.check_logits(ex * (1 + 3e-3), ex, "bf16")
 
 
+def test_score_allowance_covers_one_bf16_step_of_z_and_no_more():
+    """The score diagnostic allows one bf16 step in one component of the
+    stored z (an fp32 accumulation order other than exact-then-round may
+    round the other way), and still catches larger errors."""
+    import torch
+    # ulp_bf16 against torch's bf16 spacing: nextafter in bf16 via the bit pattern
+    x = np.array([1.0, -1.5976550329942256, 0.06, 3.0e-3, 200.0])
+    xb = torch.tensor(x, dtype=torch.float64).to(torch.bfloat16)
+    nxt = (xb.view(torch.int16) + 1).view(torch.bfloat16).to(torch.float64)
+    spacing = (nxt - xb.to(torch.float64)).abs().numpy()
+    assert np.array_equal(compare.ulp_bf16(xb.to(torch.float64).numpy()), spacing)
+    assert compare.ulp_bf16(np.array([0.0]))[0] == 0.0
+    inp = gen.make_custom(3000, 512, 64, 1, "bf16", seed=21)
+    lr = oracle.lowrank_head(inp["Q"], inp["P"], None, inp["H"], 16, "bf16", keep_scores=True)
+    z, s, idx = lr["z"][0], lr["s"][0], lr["idx"][0]
+    P = oracle.to_f64(inp["P"], "bf16")
+    allow = compare.z_step_allowance(P[idx], z, "bf16")
+    smax = float(np.max(np.abs(s)))
+    # the component whose single step moves the candidates' scores most
+    j = int(np.argmax(np.max(np.abs(P[idx]) * compare.ulp_bf16(z)[None, :], axis=0)))
+    for steps, ok in ((1, True), (-1, True), (4, False)):
+        z2 = z.copy()
+        z2[j] += steps * compare.ulp_bf16(z[j:j + 1])[0]
+        got = P[idx] @ z2
+        errs = compare.check_scores(got, s[idx], smax, "bf16", allow)
+        assert (errs == []) == ok, (steps, errs)
+    # without the allowance the one-step case is not always within the base tolerance
+    z2 = z.copy(); z2[j] += compare.ulp_bf16(z[j:j + 1])[0]
+    assert np.max(np.abs(P[idx] @ z2 - s[idx])) <= compare.SCORE_TOL["bf16"] * smax + np.max(allow)
+    assert compare.z_step_allowance(P[idx], z, "fp32").max() == 0.0
+
+
 def test_selection_stats_hand_row():
     s = np.array([-5.0, 1.0, 2.0, 1.0])
     idx = oracle.topk_order(s, 2)
