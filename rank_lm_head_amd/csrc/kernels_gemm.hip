@@ -317,26 +317,28 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
 }
 
 // --------------------------------------------------------- per-row bound
-// theta[b] = the k-th largest tile maximum of row b (or a slightly lower
-// value that between k and `cap` maxima reach); -inf when fewer than k
-// tiles exist. One wave per row.
-constexpr int kThetaE = kMaxSampleTiles / kWave;
-
+// theta[b] = a value that between k and `cap` tile maxima of row b reach
+// (at most the k-th largest maximum); -inf when fewer than k tiles exist.
+// One wave per row, kThetaE maxima per lane.
+template <int kThetaE>
 __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ tmax, int ns_tiles, int64_t B, int k,
                                                      int cap, float* __restrict__ theta) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= B) return;
   const float* t = tmax + row * ns_tiles;
+  // all loads first (clamped, branch-free), then the keys
+  float mv[kThetaE];
+#pragma unroll
+  for (int e = 0; e < kThetaE; ++e) mv[e] = t[min(e * kWave + lane, ns_tiles - 1)];
   uint64_t key[kThetaE];
   float vmin = __builtin_inff();
 #pragma unroll
   for (int e = 0; e < kThetaE; ++e) {
     const int j = e * kWave + lane;
-    const float m = t[j < ns_tiles ? j : ns_tiles - 1];
-    const bool ok = j < ns_tiles && m > neg_inf();
-    key[e] = ok ? cand_key(m, j) : 0ull;
-    if (ok) vmin = fminf(vmin, m);
+    const bool ok = j < ns_tiles && mv[e] > neg_inf();
+    key[e] = ok ? cand_key(mv[e], j) : 0ull;
+    vmin = ok ? fminf(vmin, mv[e]) : vmin;
   }
   int valid = 0;
 #pragma unroll
@@ -444,15 +446,19 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // their scores, 8 independent loads per lane at a time
-    uint64_t key[kColE];
+    // their scores: all ids from LDS, then all loads, then the keys
+    int vv[kColE];
 #pragma unroll
     for (int e = 0; e < kColE; ++e) {
       const int j = e * kWave + lane;
-      const int v = j < n ? m.vid[j] : 0;
-      const float x = sr[v];
-      key[e] = j < n ? cand_key(x, v) : 0ull;
+      vv[e] = j < n ? m.vid[j] : 0;
     }
+    float xs[kColE];
+#pragma unroll
+    for (int e = 0; e < kColE; ++e) xs[e] = sr[vv[e]];
+    uint64_t key[kColE];
+#pragma unroll
+    for (int e = 0; e < kColE; ++e) key[e] = e * kWave + lane < n ? cand_key(xs[e], vv[e]) : 0ull;
     if (C <= kColCap) {
       // one round: straight to the output
       wave_topk_emit<kColE>(key, k, m.tmp, m.ls[1], m.li[1]);
@@ -544,9 +550,19 @@ hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, in
   hipError_t e = run_gemm<C>(kModeMax, M, X, V, K, B, p.ns, p.stride, w.tmax, p.ns_tiles, nullptr, nullptr, 0,
                              nullptr, 0, stream);
   if (e != hipSuccess) return e;
-  const int cap = min(kWave, k + max(8, k / 4));
-  hipLaunchKernelGGL(theta_kernel, dim3((unsigned)((B + 3) / 4)), dim3(256), 0, stream, w.tmax, p.ns_tiles, B, k,
-                     cap, w.theta);
+  // the bound need not be the exact k-th maximum: any value that between k
+  // and cap maxima reach is valid (a looser one flags more scores)
+  const int cap = k + max(8, k / 4);
+  const dim3 tg((unsigned)((B + 3) / 4)), tb(256);
+  const int te = (p.ns_tiles + kWave - 1) / kWave;
+  if (te <= 8)
+    hipLaunchKernelGGL(theta_kernel<8>, tg, tb, 0, stream, w.tmax, p.ns_tiles, B, k, cap, w.theta);
+  else if (te <= 16)
+    hipLaunchKernelGGL(theta_kernel<16>, tg, tb, 0, stream, w.tmax, p.ns_tiles, B, k, cap, w.theta);
+  else if (te <= 24)
+    hipLaunchKernelGGL(theta_kernel<24>, tg, tb, 0, stream, w.tmax, p.ns_tiles, B, k, cap, w.theta);
+  else
+    hipLaunchKernelGGL(theta_kernel<32>, tg, tb, 0, stream, w.tmax, p.ns_tiles, B, k, cap, w.theta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   e = run_gemm<C>(kModeFilter, M, X, V, K, B, (int)p.nvb, 1, nullptr, 0, w.theta, w.S, p.ldS, w.mask, p.NW,
                   stream, t);

@@ -23,16 +23,25 @@ constexpr int kWaves = 4;
 constexpr int kMergeAt = kBuf - kTile;   // one tile adds <= 16 per column
 constexpr int kUnroll = 8;               // k steps whose loads are issued together
 
-// Loads of operand rows for kUnroll k steps starting at k0.
+// Loads of operand rows for kUnroll k steps starting at k0. `p` is a valid
+// row (callers clamp missing rows); columns past K read a clamped address
+// and are zeroed, so no load is predicated and all of them are in flight
+// together.
 template <typename T>
 __device__ __forceinline__ void load_steps(const T* __restrict__ p, bool ok, int K, int k0, u32x4* v) {
   constexpr int step = sizeof(T) == 2 ? 32 : 16;
   constexpr int per = 16 / sizeof(T);
   const int g = (threadIdx.x & 63) >> 4;
+  u32x4 x[kUnroll];
 #pragma unroll
   for (int t = 0; t < kUnroll; ++t) {
     const int kk = k0 + t * step + g * per;
-    v[t] = (ok && kk < K) ? load16(p + kk) : u32x4{0u, 0u, 0u, 0u};
+    x[t] = load16(p + (kk < K ? kk : K - per));
+  }
+#pragma unroll
+  for (int t = 0; t < kUnroll; ++t) {
+    const int kk = k0 + t * step + g * per;
+    v[t] = (ok && kk < K) ? x[t] : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -63,11 +72,12 @@ __device__ __forceinline__ f32x4 tile_dot_unrolled(const T* __restrict__ a, bool
 }
 
 // ------------------------------------------------------------ down-projection
-// Block: 16 rows of Q x 16 rows of H; the 4 waves split d and add up in LDS.
-template <typename T>
-__global__ void __launch_bounds__(256) down_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ H, int r,
-                                                        int d, int64_t B, T* __restrict__ Z) {
-  __shared__ f32x4 red[kWaves][kWave];
+// Block: 16 rows of Q x 16 rows of H; NW waves split d and add up in LDS
+// (16 waves for long rows, so that each wave's loads are few round trips).
+template <typename T, int NW>
+__global__ void __launch_bounds__(NW * 64) down_mfma_kernel(const T* __restrict__ Q, const T* __restrict__ H, int r,
+                                                            int d, int64_t B, T* __restrict__ Z) {
+  __shared__ f32x4 red[NW][kWave];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, g = lane >> 4;
   const int j0 = blockIdx.x * kTile;
@@ -75,7 +85,7 @@ __global__ void __launch_bounds__(256) down_mfma_kernel(const T* __restrict__ Q,
   const int qrow = j0 + col;
   const int64_t hrow = b0 + col;
   const bool q_ok = qrow < r, h_ok = hrow < B;
-  const int per = ((d + kWaves - 1) / kWaves + 31) / 32 * 32;
+  const int per = ((d + NW - 1) / NW + 31) / 32 * 32;
   const int kb = min(d, wave * per), ke = min(d, kb + per);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   acc = tile_dot_unrolled<T>(Q + (int64_t)(q_ok ? qrow : 0) * d + kb, q_ok,
@@ -85,7 +95,7 @@ __global__ void __launch_bounds__(256) down_mfma_kernel(const T* __restrict__ Q,
   if (wave == 0) {
     f32x4 sum = red[0][lane];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) sum += red[w][lane];
+    for (int w = 1; w < NW; ++w) sum += red[w][lane];
     if (h_ok) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -258,8 +268,12 @@ int plan_vsplit(int64_t B, int64_t V) {
 hipError_t launch_down(int dtype, const void* Q, const void* H, int r, int d, int64_t B, void* Z,
                        hipStream_t stream) {
   dim3 grid((r + kTile - 1) / kTile, (unsigned)((B + kTile - 1) / kTile));
-  LRH_DISPATCH(dtype, hipLaunchKernelGGL(down_mfma_kernel<T>, grid, dim3(256), 0, stream, (const T*)Q,
-                                         (const T*)H, r, d, B, (T*)Z));
+  if (d >= 2048)
+    LRH_DISPATCH(dtype, hipLaunchKernelGGL((down_mfma_kernel<T, 16>), grid, dim3(16 * 64), 0, stream, (const T*)Q,
+                                           (const T*)H, r, d, B, (T*)Z));
+  else
+    LRH_DISPATCH(dtype, hipLaunchKernelGGL((down_mfma_kernel<T, 4>), grid, dim3(4 * 64), 0, stream, (const T*)Q,
+                                           (const T*)H, r, d, B, (T*)Z));
   return hipGetLastError();
 }
 
