@@ -268,6 +268,28 @@ def main() -> int:
     us_full = t_full / ((KB + 3) // 4 * 4) * 1e6
     full_sel_s = event_timed(torch, hip, heads[:1], full, min(KB, 200))
 
+    # vendor context: the library GEMM (hipBLASLt through torch) for all V
+    # logits of the full head on the same rows, without any selection
+    vendor = None
+    if cfg.dtype == "bf16":
+        Hb = dsets[0]["H"]
+        lin = torch.nn.functional.linear
+        for _ in range(2):
+            lin(Hb, W)
+        torch.cuda.synchronize()
+        reps = max(2, min(50, int(2e5 // max(1.0, us_full))))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            lin(Hb, W)
+        e1.record()
+        torch.cuda.synchronize()
+        v_us = e0.elapsed_time(e1) / reps * 1e3
+        vendor = {"op": "torch.nn.functional.linear(H, W): all V logits of the full head, bf16 out, no selection",
+                  "us_per_call": v_us, "tflops": 2.0 * cfg.B * cfg.V * cfg.d / v_us / 1e6,
+                  "hbm_frac": (cfg.V * cfg.d * s + cfg.B * cfg.d * s + cfg.B * cfg.V * s) / (v_us * 1e-6)
+                              / (HBM_PEAK_GBS * 1e9)}
+
     # roofline of the dominant kernel: the vocabulary score pass. Algorithmic
     # work per launch: every P row once (V units of r*s bytes) plus the B rows
     # of z, and 2*B*r flops per vocabulary row. Small batches stream P on the
@@ -326,7 +348,8 @@ def main() -> int:
         "full_head": {"us_per_call": us_full, "speedup_of_draft_head": us_full / us_cold,
                       "select_us_per_launch": full_sel_s * 1e6,
                       "hbm_frac": full_bytes / (full_sel_s) / (HBM_PEAK_GBS * 1e9),
-                      "mfma_frac": 2.0 * cfg.B * cfg.V * cfg.d / full_sel_s / peak_flops},
+                      "mfma_frac": 2.0 * cfg.B * cfg.V * cfg.d / full_sel_s / peak_flops,
+                      "vendor_gemm_context": vendor},
     }
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20

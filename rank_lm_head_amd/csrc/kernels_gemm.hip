@@ -43,12 +43,12 @@ constexpr int kGemmThreads = 256;
 constexpr int kBK = 64;                  // K elements per LDS stage
 constexpr int kRowChunks = kBK / 8;      // 16-byte chunks per row per stage
 constexpr int kXcds = 8;
-constexpr int kStages = 3;               // LDS stage buffers
 constexpr int kMaxSampleTiles = 2048;    // tile maxima per row kept by the sample pass
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int ST_ = 3>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int ST = ST_;                     // LDS stage buffers (ST - 1 stages in flight)
   static constexpr int TM = BM / WM, TN = BN / WN;   // wave tile
   static constexpr int FM = TM / 16, FN = TN / 16;   // 16x16 tiles per wave
   static constexpr int A_LD = BM * kRowChunks / kGemmThreads;
@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
     int64_t ldS, uint32_t* __restrict__ mask, int NW) {
   extern __shared__ u32x4 lds[];
   constexpr int SA = C::BM * kRowChunks, SB = C::BN * kRowChunks;   // 16-byte chunks per stage
-  const int nbuf = min(kStages, (K + kBK - 1) / kBK);   // stage buffers (fewer for short K)
+  const int nbuf = min(C::ST, (K + kBK - 1) / kBK);   // stage buffers (fewer for short K)
   u32x4* As = lds;                  // [nbuf][SA]
   u32x4* Bs = lds + nbuf * SA;      // [nbuf][SB]
 
@@ -187,24 +187,29 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
   StageDma<C::B_LD> lb;
   la.init(M, m0, V, K);
   lb.init(X, n0, B, K);
-  // Stages kc live in buffer kc % 3; two are in flight while one is used.
-  la.issue(As, 0, K, ktail && nk == 1);
-  lb.issue(Bs, 0, K, ktail && nk == 1);
-  if (nk > 1) {
-    la.issue(As + SA, 1, K, ktail && nk == 2);
-    lb.issue(Bs + SB, 1, K, ktail && nk == 2);
+  // Stage kc lives in buffer kc % nbuf; ST - 1 stages are in flight while
+  // one is used.
+  static_assert(C::ST == 2 || C::ST == 3, "two or three stage buffers");
+#pragma unroll
+  for (int st = 0; st < C::ST - 1; ++st) {
+    if (st < nk) {
+      la.issue(As + st * SA, st, K, ktail && st == nk - 1);
+      lb.issue(Bs + st * SB, st, K, ktail && st == nk - 1);
+    }
   }
   for (int kc = 0; kc < nk; ++kc) {
-    // this wave's copies of stage kc are done once only stage kc+1's remain
-    if (kc + 1 < nk)
-      wait_vmcnt<C::A_LD + C::B_LD>();
+    // this wave's copies of stage kc are done once only the later stages'
+    // (ST - 2 of them, fewer at the end) remain
+    if (C::ST == 3 && kc + 1 < nk)
+      wait_vmcnt<(C::ST == 3 ? C::A_LD + C::B_LD : 0)>();
     else
       wait_vmcnt<0>();
     lds_barrier();     // every wave's copies of stage kc landed; stage kc-1 is no longer read
-    if (kc + 2 < nk) {
-      const int nb = (kc + 2) % nbuf;
-      la.issue(As + nb * SA, kc + 2, K, ktail && kc + 2 == nk - 1);
-      lb.issue(Bs + nb * SB, kc + 2, K, ktail && kc + 2 == nk - 1);
+    if (kc + C::ST - 1 < nk) {
+      const int nx = kc + C::ST - 1;
+      const int nb = nx % nbuf;
+      la.issue(As + nb * SA, nx, K, ktail && nx == nk - 1);
+      lb.issue(Bs + nb * SB, nx, K, ktail && nx == nk - 1);
     }
     const u32x4* as = As + (kc % nbuf) * SA;
     const u32x4* bs = Bs + (kc % nbuf) * SB;
@@ -489,7 +494,8 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
 
 namespace {
 
-using CfgWide = GemmCfg<256, 128, 2, 2>;    // B > 64
+using CfgBig = GemmCfg<256, 256, 2, 2, 2>;  // B > 128: 128x128 per wave, two stage buffers (LDS)
+using CfgWide = GemmCfg<256, 128, 2, 2>;    // 64 < B <= 128
 using CfgNarrow = GemmCfg<256, 64, 4, 1>;   // B <= 64
 using CfgDown = GemmCfg<64, 64, 2, 2>;      // z = Q . h for many rows (r is small)
 
@@ -510,7 +516,7 @@ int sample_stride(int64_t V, int k) {
 template <class C>
 size_t gemm_lds_bytes(int K = 1 << 30) {
   const int nk = (K + kBK - 1) / kBK;
-  return size_t(nk < kStages ? nk : kStages) * (C::BM + C::BN) * kRowChunks * sizeof(u32x4);
+  return size_t(nk < C::ST ? nk : C::ST) * (C::BM + C::BN) * kRowChunks * sizeof(u32x4);
 }
 
 template <class C>
@@ -578,6 +584,7 @@ bool batch_path(int dtype, int64_t B) { return dtype == 0 && B > kSmallB; }
 
 hipError_t batch_init() {
   hipError_t e = allow_lds<CfgWide>();
+  if (e == hipSuccess) e = allow_lds<CfgBig>();
   if (e == hipSuccess) e = allow_lds<CfgNarrow>();
   if (e == hipSuccess) e = allow_lds<CfgDown>();
   return e;
@@ -633,7 +640,9 @@ hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, i
   const uint16_t* m = static_cast<const uint16_t*>(M);
   const uint16_t* x = static_cast<const uint16_t*>(X);
   if (B <= 64) return run_pass<CfgNarrow>(p, m, x, V, K, B, k, w, idx, score, stream, t);
-  return run_pass<CfgWide>(p, m, x, V, K, B, k, w, idx, score, stream, t);
+  if (B <= 128) return run_pass<CfgWide>(p, m, x, V, K, B, k, w, idx, score, stream, t);
+  static_assert(CfgBig::TM == CfgWide::TM, "one mask layout above 64 rows");
+  return run_pass<CfgBig>(p, m, x, V, K, B, k, w, idx, score, stream, t);
 }
 
 }  // namespace lrh
