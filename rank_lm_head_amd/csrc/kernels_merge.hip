@@ -90,6 +90,7 @@ constexpr int kCandE = 8;                   // candidates per lane of wave 0
 constexpr int kCandSlots = kCandE * kWave;
 constexpr int kHeadE = kMaxLists / kWave;   // list heads per lane of wave 0
 constexpr int kFront = 4;                   // leading entries of each list read up front
+constexpr int kRawPerLane = 8;              // a slice's raw scores per lane (slices <= 512 rows)
 
 struct MergeSmem {
   uint64_t heads[kMaxLists];
@@ -101,6 +102,7 @@ struct MergeSmem {
   float top_s[kWave];
   int top_i[kWave];
   int deep[kMaxLists];       // lists whose front entries all reach the bound
+  uint64_t deep_key[kMaxLists];   // and the key of their last front entry
   uint64_t T;
   int n_cand;
   int n_deep;
@@ -158,8 +160,8 @@ __device__ __forceinline__ void select_candidates(MergeSmem& m, int nc, int k) {
 //     candidates, wave w of block g rescores winner g*per + w instead.
 template <typename T, bool RESCORE>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
-    const float* __restrict__ part_s, const int* __restrict__ part_i, int n, int64_t V, int k,
-    const T* __restrict__ W, const T* __restrict__ H, int d, int32_t* __restrict__ idx,
+    const float* __restrict__ part_s, const int* __restrict__ part_i, int n, int L, const float* __restrict__ raw,
+    int64_t V, int k, const T* __restrict__ W, const T* __restrict__ H, int d, int32_t* __restrict__ idx,
     float* __restrict__ score, float* __restrict__ logits) {
   __shared__ MergeSmem m;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -168,17 +170,18 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
 
   // 1. the first kFront entries of every list (contiguous across lists in
   //    the depth-major layout), one list per thread; heads to LDS
-  const int64_t R = b * (int64_t)k * n;   // row base
+  const int64_t R = b * (int64_t)L * n;   // row base
+  const int F = min(kFront, L);           // front entries held
   const int p = threadIdx.x;
   const int pc = min(p, n - 1);
   float fs[kFront];
   int fi[kFront];
 #pragma unroll
   for (int j = 0; j < kFront; ++j) {
-    const int jc = min(j, k - 1);
+    const int jc = min(j, L - 1);
     fs[j] = part_s[R + (int64_t)jc * n + pc];
     fi[j] = part_i[R + (int64_t)jc * n + pc];
-    if (p >= n || j >= k) fi[j] = kSentinelId;
+    if (p >= n || j >= L) fi[j] = kSentinelId;
   }
   if (p < n) m.heads[p] = fi[0] != kSentinelId ? cand_key(fs[0], fi[0]) : 0ull;
   if (threadIdx.x == 0) {
@@ -236,27 +239,57 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
         ++slot;
       }
     }
-    // a list whose last front entry reaches the bound may hold more
-    if (k > kFront && (pass >> (kFront - 1)) & 1u) m.deep[atomicAdd(&m.n_deep, 1)] = p;
+    // a slice whose last front entry reaches the bound may hold more: the
+    // rest of its list (L > F), or its raw scores (lists shorter than k)
+    const bool more = L > F || (L < k && raw != nullptr);
+    if (more && (pass >> (F - 1)) & 1u) {
+      const int dl = atomicAdd(&m.n_deep, 1);
+      m.deep[dl] = p;
+      m.deep_key[dl] = cand_key(fs[F - 1], fi[F - 1]);
+    }
   }
   __syncthreads();
   if (m.n_deep > 0) {
-    // rare: the rest of those lists, one list per wave at a time
+    // rare: one slice per wave at a time
     const int nd = m.n_deep;
     for (int dl = wave; dl < nd; dl += kMergeWaves) {
       const int q = m.deep[dl];
-      const int j = kFront + lane;
-      const int jc = min(j, k - 1);
-      const float sc = part_s[R + (int64_t)jc * n + q];
-      const int id = j < k ? part_i[R + (int64_t)jc * n + q] : kSentinelId;
-      const bool ps = reaches(sc, id);
-      const unsigned long long mk = __ballot(ps);
-      if (mk) {
-        int base = 0;
-        if (lane == 0) base = atomicAdd(&m.n_cand, __popcll(mk));
-        base = __shfl(base, 0);
-        const int slot = base + lanes_below(mk);
-        if (ps && slot < kCandSlots) m.cand[slot] = cand_key(sc, id);
+      if (L > F) {
+        const int j = F + lane;
+        const int jc = min(j, L - 1);
+        const float sc = part_s[R + (int64_t)jc * n + q];
+        const int id = j < L ? part_i[R + (int64_t)jc * n + q] : kSentinelId;
+        const bool ps = reaches(sc, id);
+        const unsigned long long mk = __ballot(ps);
+        if (mk) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&m.n_cand, __popcll(mk));
+          base = __shfl(base, 0);
+          const int slot = base + lanes_below(mk);
+          if (ps && slot < kCandSlots) m.cand[slot] = cand_key(sc, id);
+        }
+      } else {
+        // the slice's raw scores below its list's last entry that reach T
+        const int64_t lo = V * q / n, hi = V * (q + 1) / n;
+        const uint64_t below = m.deep_key[dl];
+        const float* rr = raw + b * V;
+        float xs[kRawPerLane];
+#pragma unroll
+        for (int t = 0; t < kRawPerLane; ++t) xs[t] = rr[min(lo + t * kWave + lane, hi - 1)];
+#pragma unroll
+        for (int t = 0; t < kRawPerLane; ++t) {
+          const int64_t v = lo + t * kWave + lane;
+          const uint64_t key = v < hi ? cand_key(xs[t], (int)v) : 0ull;
+          const bool ps = key != 0 && key < below && reaches(xs[t], (int)v);
+          const unsigned long long mk = __ballot(ps);
+          if (mk) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&m.n_cand, __popcll(mk));
+            base = __shfl(base, 0);
+            const int slot = base + lanes_below(mk);
+            if (ps && slot < kCandSlots) m.cand[slot] = key;
+          }
+        }
       }
     }
     __syncthreads();
@@ -269,12 +302,31 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
   if (wave == 0) {
     if (fits) {
       select_candidates(m, nc, k);
-    } else {
+    } else if (L == k) {
       float s;
       int i;
       merge_lists_seq(part_s + R, part_i + R, n, k, s, i);
       m.top_s[lane] = s;
       m.top_i[lane] = i;
+    } else {
+      // ties flag too many candidates: the k best of the row's raw scores,
+      // 448 at a time, each chunk merged into the running best
+      m.top_s[lane] = neg_inf();
+      m.top_i[lane] = kSentinelId;
+      const float* rr = raw + b * V;
+      for (int64_t c0 = 0; c0 < V; c0 += 7 * kWave) {
+        uint64_t key[8];
+#pragma unroll
+        for (int e = 0; e < 7; ++e) {
+          const int64_t v = c0 + e * kWave + lane;
+          key[e] = v < V ? cand_key(rr[v], (int)v) : 0ull;
+        }
+        key[7] = lane < k && m.top_i[lane] != kSentinelId ? cand_key(m.top_s[lane], m.top_i[lane]) : 0ull;
+        wave_topk_emit<8>(key, k, m.tmp, m.top_s, m.top_i);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
     }
   } else if (spec) {
     // this block's candidates in slot order; the t-th goes to wave 1 + t % 7
@@ -339,14 +391,15 @@ hipError_t launch_rescore(int dtype, const void* W, const void* H, const int32_t
   return hipGetLastError();
 }
 
-hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int64_t V,
-                        int64_t B, int k, const void* W, const void* H, int d, int32_t* idx, float* score,
-                        float* logits, hipStream_t stream) {
-  if (n < 1 || n > kMaxLists) return hipErrorInvalidValue;
+hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, const float* raw,
+                        int64_t V, int64_t B, int k, const void* W, const void* H, int d, int32_t* idx,
+                        float* score, float* logits, hipStream_t stream) {
+  if (n < 1 || n > kMaxLists || L < 1 || L > k) return hipErrorInvalidValue;
+  if (L < k && (!raw || (V + n - 1) / n > kRawPerLane * kWave)) return hipErrorInvalidValue;
   const dim3 block(kMergeThreads);
   if (!logits) {
     const dim3 grid(1, (unsigned)B);
-    hipLaunchKernelGGL((merge_kernel<uint16_t, false>), grid, block, 0, stream, part_s, part_i, n, V, k,
+    hipLaunchKernelGGL((merge_kernel<uint16_t, false>), grid, block, 0, stream, part_s, part_i, n, L, raw, V, k,
                        (const uint16_t*)nullptr, (const uint16_t*)nullptr, d, idx, score, logits);
     return hipGetLastError();
   }
@@ -354,10 +407,10 @@ hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n
   const int G = (2 * k + kMergeWaves - 2) / (kMergeWaves - 1);
   const dim3 grid((unsigned)G, (unsigned)B);
   if (dtype == 0)
-    hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, block, 0, stream, part_s, part_i, n, V, k,
+    hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, block, 0, stream, part_s, part_i, n, L, raw, V, k,
                        (const uint16_t*)W, (const uint16_t*)H, d, idx, score, logits);
   else
-    hipLaunchKernelGGL((merge_kernel<float, true>), grid, block, 0, stream, part_s, part_i, n, V, k,
+    hipLaunchKernelGGL((merge_kernel<float, true>), grid, block, 0, stream, part_s, part_i, n, L, raw, V, k,
                        (const float*)W, (const float*)H, d, idx, score, logits);
   return hipGetLastError();
 }

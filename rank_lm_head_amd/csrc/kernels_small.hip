@@ -102,23 +102,24 @@ __device__ __forceinline__ void finish_block(SmallLds<NB>& sm, WaveSel<NB>& st, 
 // KiB of consecutive rows. Block x owns the contiguous slice
 // [V*x/n, V*(x+1)/n) (at most kBlockRows rows) and each wave a quarter of
 // it; the next U wave loads are issued before the current ones are used.
-// The scores go to LDS, and after the pass wave b finds the k best of the
-// slice for row b (windowed bisection and counting ranks, topk.h) and writes
-// them, in order: entry j to part_[b][j][x] (depth-major, so that the first
-// entries of all lists are contiguous for the merge).
+// The scores go to LDS. After the pass the block copies them to raw[b][v]
+// (coalesced) and wave b writes the L best of the slice for row b, in
+// order, entry j to part_[b][j][x] (depth-major, so that the leading entries
+// of all lists are contiguous for the merge). L is small (min(4, k)): the
+// merge needs more of a slice only when its L-th entry still reaches the
+// merge's bound, and then reads the slice's raw scores.
 constexpr int kBlockRows = 512;
 
 template <int K, int NB, int E>
 __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
-    const uint16_t* __restrict__ M, const uint16_t* __restrict__ X, int64_t V, int B, int k,
-    float* __restrict__ part_s, int* __restrict__ part_i) {
+    const uint16_t* __restrict__ M, const uint16_t* __restrict__ X, int64_t V, int B, int L,
+    float* __restrict__ part_s, int* __restrict__ part_i, float* __restrict__ raw) {
   constexpr int LPR = K / 8;
   constexpr int RPL = kWave / LPR;
   constexpr int U = 8;
   constexpr int STEP = U * RPL;
   static_assert(K % 8 == 0 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "row length");
   __shared__ float sc[NB][E * kWave];
-  __shared__ uint64_t tmp[NB][kWave];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = lane % LPR, sub = lane / LPR;
 
@@ -162,17 +163,22 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
     for (int t = 0; t < U; ++t) cur[t] = nxt[t];
   }
   __syncthreads();
+  const int nrows = (int)(bhi - blo);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b >= B) break;
+    for (int j = threadIdx.x; j < nrows; j += kSmallThreads) raw[(int64_t)b * V + blo + j] = sc[b][j];
+  }
   if (wave < B) {
     const int b = wave;
-    const int nrows = (int)(bhi - blo);
     uint64_t key[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = e * kWave + lane;
       key[e] = j < nrows ? cand_key(sc[b][j], (int)(blo + j)) : 0ull;
     }
-    const int64_t o = (int64_t)b * k * nblk + blockIdx.x;
-    wave_topk_emit<E>(key, k, tmp[b], part_s + o, part_i + o, nblk);
+    const int64_t o = (int64_t)b * L * nblk + blockIdx.x;
+    wave_top_argmax<E>(key, L, part_s + o, part_i + o, nblk);
   }
 }
 
@@ -305,35 +311,38 @@ hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t
   return hipGetLastError();
 }
 
+int small_list_len(int k) { return k < kSliceList ? k : kSliceList; }
+
 template <int K>
 static hipError_t launch_short_k(const void* M, const void* X, int64_t V, int64_t B, int k, float* ps, int* pi,
-                                 hipStream_t stream, Timing t) {
+                                 float* raw, hipStream_t stream, Timing t) {
   const int nblk = small_blocks(V);
   dim3 grid(nblk);
   const int64_t rows = (V + nblk - 1) / nblk;   // most rows of one block
+  const int L = small_list_len(k);
   if (rows <= 4 * kWave) {
     LRH_NB_DISPATCH(B, LRH_LAUNCH(t, (select_short_kernel<K, NB, 4>), grid, dim3(kSmallThreads), 0, stream,
-                                  (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
+                                  (const uint16_t*)M, (const uint16_t*)X, V, (int)B, L, ps, pi, raw));
   } else if (rows <= 5 * kWave) {
     LRH_NB_DISPATCH(B, LRH_LAUNCH(t, (select_short_kernel<K, NB, 5>), grid, dim3(kSmallThreads), 0, stream,
-                                  (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
+                                  (const uint16_t*)M, (const uint16_t*)X, V, (int)B, L, ps, pi, raw));
   } else {
     LRH_NB_DISPATCH(B, LRH_LAUNCH(t, (select_short_kernel<K, NB, 8>), grid, dim3(kSmallThreads), 0, stream,
-                                  (const uint16_t*)M, (const uint16_t*)X, V, (int)B, k, ps, pi));
+                                  (const uint16_t*)M, (const uint16_t*)X, V, (int)B, L, ps, pi, raw));
   }
   return hipGetLastError();
 }
 
 hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* ps,
-                               int* pi, hipStream_t stream, Timing t) {
+                               int* pi, float* raw, hipStream_t stream, Timing t) {
   switch (K) {
-    case 8: return launch_short_k<8>(M, X, V, B, k, ps, pi, stream, t);
-    case 16: return launch_short_k<16>(M, X, V, B, k, ps, pi, stream, t);
-    case 32: return launch_short_k<32>(M, X, V, B, k, ps, pi, stream, t);
-    case 64: return launch_short_k<64>(M, X, V, B, k, ps, pi, stream, t);
-    case 128: return launch_short_k<128>(M, X, V, B, k, ps, pi, stream, t);
-    case 256: return launch_short_k<256>(M, X, V, B, k, ps, pi, stream, t);
-    case 512: return launch_short_k<512>(M, X, V, B, k, ps, pi, stream, t);
+    case 8: return launch_short_k<8>(M, X, V, B, k, ps, pi, raw, stream, t);
+    case 16: return launch_short_k<16>(M, X, V, B, k, ps, pi, raw, stream, t);
+    case 32: return launch_short_k<32>(M, X, V, B, k, ps, pi, raw, stream, t);
+    case 64: return launch_short_k<64>(M, X, V, B, k, ps, pi, raw, stream, t);
+    case 128: return launch_short_k<128>(M, X, V, B, k, ps, pi, raw, stream, t);
+    case 256: return launch_short_k<256>(M, X, V, B, k, ps, pi, raw, stream, t);
+    case 512: return launch_short_k<512>(M, X, V, B, k, ps, pi, raw, stream, t);
     default: return hipErrorInvalidValue;
   }
 }

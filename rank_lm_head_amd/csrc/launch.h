@@ -37,10 +37,13 @@ bool small_long_path(int dtype, int64_t B, int64_t K, int64_t V);
 
 // z = round(Q . h) for B <= 4 rows.
 hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream);
-// Streaming score pass: per block, the k best of its slice for each row,
-// written depth-major: entry j of block x's list at part_[row][j][x].
+// Streaming score pass: per block, the small_list_len(k) best of its slice
+// for each row, written depth-major (entry j of block x's list at
+// part_[row][j][x]), and every score to raw[row][v] (B x V).
+constexpr int kSliceList = 4;
+int small_list_len(int k);
 hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
-                               int* part_i, hipStream_t stream, Timing t = {});
+                               int* part_i, float* raw, hipStream_t stream, Timing t = {});
 hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
                               int* part_i, hipStream_t stream, Timing t = {});
 
@@ -98,12 +101,15 @@ hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, i
                                Timing t = {});
 
 // ----------------------------------------------------- kernels_merge.hip
-// Merges n sorted lists of k per row (part_[row][entry][list], n <= 512) into
-// idx / score (score may be NULL). With logits != NULL, also writes the
-// winners' exact logits W[id] . h_b.
-hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int64_t V, int64_t B, int k,
-                        const void* W, const void* H, int d, int32_t* idx, float* score, float* logits,
-                        hipStream_t stream);
+// Merges n sorted lists of L entries per row (part_[row][entry][list],
+// n <= 512) into the k best, to idx / score (score may be NULL). Lists
+// shorter than k (L < k) come with the rows' raw scores (raw[row][v], list p
+// holding the best of the slice [V*p/n, V*(p+1)/n)); with L == k, raw may be
+// NULL. With logits != NULL, also writes the winners' exact logits
+// W[id] . h_b.
+hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, const float* raw,
+                        int64_t V, int64_t B, int k, const void* W, const void* H, int d, int32_t* idx,
+                        float* score, float* logits, hipStream_t stream);
 
 // logits[b, j] = W[idx[b, j], :] . h_b (NaN for ids outside [0, V)).
 hipError_t launch_rescore(int dtype, const void* W, const void* H, const int32_t* idx, int64_t B,

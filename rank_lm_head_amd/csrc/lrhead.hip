@@ -28,6 +28,7 @@ struct lrhead_s {
   void* z;          // B_max x r, weight dtype
   float* part_s;    // candidate lists: rows x slices x k_max
   int* part_i;
+  float* raw;       // raw scores of the streaming path: min(B_max, 4) x V
   bool batch;       // bf16 with B_max > 4: the GEMM path's scratch exists
   lrh::BatchScratch bw;
   hipEvent_t ev_before;  // optional events attached to the score pass: its start
@@ -59,7 +60,7 @@ size_t elem_bytes(int dtype) { return dtype == LRHEAD_BF16 ? 2 : 4; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t z, part_s, part_i, batch, total;
+  size_t z, part_s, part_i, raw, batch, total;
 };
 
 // Most candidate lists any call with B <= B_max writes (B x slices), over
@@ -85,7 +86,10 @@ Layout layout(int dtype, int64_t V, int64_t r, int64_t B_max, int k_max) {
   const size_t lists = align256(size_t(max_list_rows(B_max, V)) * size_t(k_max) * 4 + 16);
   L.part_s = zb;
   L.part_i = zb + lists;
-  L.batch = zb + 2 * lists;
+  // raw scores of the streaming path (bf16 heads, B <= kSmallB rows)
+  const int64_t raw_rows = dtype == LRHEAD_BF16 ? (B_max < lrh::kSmallB ? B_max : lrh::kSmallB) : 0;
+  L.raw = zb + 2 * lists;
+  L.batch = L.raw + align256(size_t(raw_rows) * size_t(V) * 4);
   L.total = L.batch;
   if (lrh::batch_path(dtype, B_max)) L.total += align256(lrh::batch_scratch_bytes(V, B_max));
   return L;
@@ -156,12 +160,16 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
       LRH_HIP(lrh::launch_rescore(h->dtype, h->W, H, idx, B, k, h->V, (int)h->d, logits, s), "rescore launch");
     return LRHEAD_OK;
   }
-  int n_lists;
+  int n_lists, list_len = k;
+  const float* raw = nullptr;
   if (lrh::small_path(h->dtype, B, h->r, h->V)) {
     LRH_HIP(lrh::launch_down_small(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
-    LRH_HIP(lrh::launch_select_small(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, s, timing(h)),
+    LRH_HIP(lrh::launch_select_small(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, h->raw, s,
+                                     timing(h)),
             "score/selection launch");
     n_lists = lrh::small_blocks(h->V);
+    list_len = lrh::small_list_len(k);
+    raw = h->raw;
   } else {
     LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
     n_lists = lrh::plan_vsplit(B, h->V);
@@ -169,8 +177,8 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
                                timing(h)),
             "score/selection launch");
   }
-  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, h->V, B, k, h->W, H, (int)h->d, idx, score,
-                            logits, s),
+  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, raw, h->V, B, k, h->W, H,
+                            (int)h->d, idx, score, logits, s),
           "merge launch");
   return LRHEAD_OK;
 }
@@ -223,6 +231,7 @@ int lrhead_create(lrhead_t* out, int dtype, int64_t V, int64_t d, int64_t r, con
   h->z = h->ws + L.z;
   h->part_s = reinterpret_cast<float*>(h->ws + L.part_s);
   h->part_i = reinterpret_cast<int*>(h->ws + L.part_i);
+  h->raw = reinterpret_cast<float*>(h->ws + L.raw);
   h->batch = lrh::batch_path(dtype, B_max);
   h->bw = h->batch ? lrh::batch_scratch(h->ws + L.batch, V, B_max) : lrh::BatchScratch{};
   h->ev_before = nullptr;
@@ -282,8 +291,8 @@ int fullhead_topk(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, flo
                                timing(h)),
             "full-head selection launch");
   }
-  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, h->V, B, k, nullptr, nullptr, (int)h->d, idx,
-                            logits, nullptr, s),
+  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, k, nullptr, h->V, B, k, nullptr, nullptr,
+                            (int)h->d, idx, logits, nullptr, s),
           "merge launch");
   return LRHEAD_OK;
 }

@@ -19,6 +19,9 @@
 //  * wave_select_threshold: the exact k-th best by a full bisection, used
 //    when ties keep the window from being reached.
 //
+//  * wave_top_argmax: the few best (a slice's leading entries) by repeated
+//    wave-wide argmax.
+//
 //  * merge_lists_seq: a wave-wide fold of sorted lists, the fallback of the
 //    merge kernel when too many entries tie at its threshold.
 #pragma once
@@ -351,6 +354,53 @@ __device__ __forceinline__ void wave_topk_emit(const uint64_t (&key)[E], int k, 
   n = min(n, kWave);
   pad_keys(tmp, n);
   wave_rank_emit(tmp, n, k, out_s, out_i, stride);
+}
+
+// ------------------------------------------------- a few best by argmax
+// Wave-wide maximum of a 64-bit key: DPP inside rows of 16 lanes, then the
+// four row results by readlane.
+template <int Ctrl>
+__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = dpp_u32<Ctrl>(hi), ol = dpp_u32<Ctrl>(lo);
+  const bool take = ((uint64_t)oh << 32 | ol) > ((uint64_t)hi << 32 | lo);
+  hi = take ? oh : hi;
+  lo = take ? ol : lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  uint32_t hi = (uint32_t)(x >> 32), lo = (uint32_t)x;
+  dpp_max_step<0xB1>(hi, lo);
+  dpp_max_step<0x4E>(hi, lo);
+  dpp_max_step<0x141>(hi, lo);
+  dpp_max_step<0x140>(hi, lo);
+  uint64_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t v = ((uint64_t)rl(hi, 16 * r) << 32) | rl(lo, 16 * r);
+    m = v > m ? v : m;
+  }
+  return m;
+}
+
+// The L best of E keys per lane (distinct where non-empty; L small), in
+// candidate order, to out_s/out_i[r * stride], r = 0 .. L-1, by L rounds of
+// a wave-wide argmax (the winning key is cleared each round). Empty ranks get
+// empty entries. The keys are consumed.
+template <int E>
+__device__ __forceinline__ void wave_top_argmax(uint64_t (&key)[E], int L, float* __restrict__ out_s,
+                                                int* __restrict__ out_i, int64_t stride) {
+  const int lane = threadIdx.x & 63;
+  for (int r = 0; r < L; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) best = key[e] > best ? key[e] : best;
+    const uint64_t w = wave_max_u64(best);
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = key[e] == w ? 0ull : key[e];
+    if (lane == 0) {
+      out_s[r * stride] = w ? key_score(w) : neg_inf();
+      out_i[r * stride] = w ? key_id(w) : kSentinelId;
+    }
+  }
 }
 
 // ------------------------------------------------------- sequential merge
