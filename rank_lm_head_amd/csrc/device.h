@@ -31,6 +31,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kSentinelId = 0x7fffffff;
 
+// The wave's index in its block, as a wave-uniform (scalar) value, so that
+// branches and loop bounds derived from it stay scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

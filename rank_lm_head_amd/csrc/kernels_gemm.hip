@@ -75,7 +75,6 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // The wave's index in the block, as a value the compiler knows to be
 // uniform (it feeds the LDS destination register of the copies).
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ uint32_t uniform_u32(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 
 template <int LD>

@@ -7,12 +7,12 @@
 // candidates cheaply, then score them exactly": the retrieved candidates are
 // scored exactly by the original full-rank head).
 //
-// Merge. Take any bound T that at least k list heads (best entries) reach.
-// Then at least k entries reach T, so an entry below T is preceded by k
-// others and cannot win, and a list whose head is below T holds no winner.
-// The kernel reads all lists of a row in one coalesced pass, finds such a T
-// among the heads (windowed bisection, topk.h), gathers the entries that
-// reach it (a few k of them) and ranks the k best of those.
+// Merge. Take any bound T that at least k list entries reach. Then an entry
+// below T is preceded by k others and cannot win, and a list whose head is
+// below T holds no winner. The kernel reads the leading entries of all lists
+// of a row in one coalesced pass, finds such a T among them (a histogram of
+// score images), gathers the entries that reach it (a few more than k) and
+// ranks the k best of those.
 //
 // Rescoring: logit = W[id, :] . h with fp32 accumulation, one wave per
 // candidate, every load of the W row and of h issued before the products.
@@ -23,7 +23,7 @@ namespace lrh {
 
 constexpr int kMergeWaves = 8;
 constexpr int kMergeThreads = kMergeWaves * kWave;
-constexpr int kMaxLists = kMergeWaves * kWave;   // heads sorted at once
+constexpr int kMaxLists = kMergeWaves * kWave;   // lists of a row (one per thread)
 
 // ------------------------------------------------------------- row dot
 template <typename T>
@@ -88,28 +88,33 @@ __global__ void __launch_bounds__(256) rescore_kernel(const T* __restrict__ W, c
 // ---------------------------------------------------------------- merge
 constexpr int kCandE = 8;                   // candidates per lane of wave 0
 constexpr int kCandSlots = kCandE * kWave;
-constexpr int kHeadE = kMaxLists / kWave;   // list heads per lane of wave 0
 constexpr int kFront = 4;                   // leading entries of each list read up front
 constexpr int kRawPerLane = 8;              // a slice's raw scores per lane (slices <= 512 rows)
 
+constexpr int kHistBins = 256;
+constexpr int kRankSlots = 2 * kWave;     // candidates ranked directly
+
 struct MergeSmem {
-  uint64_t heads[kMaxLists];
+  uint32_t hist[kHistBins];   // front entries per bin of score images
+  uint32_t wmin[kMergeWaves], wmax[kMergeWaves];
+  int wcnt[kMergeWaves];
   uint64_t cand[kCandSlots];
   float spec[kCandSlots];   // exact logit of candidate slot j (this block's share)
   int slot_of[kWave];       // candidate slot of each winner
-  uint64_t tmp[kWave];
-  int tslot[kWave];
+  uint64_t tmp[kRankSlots];
+  int tslot[kRankSlots];
   float top_s[kWave];
   int top_i[kWave];
   int deep[kMaxLists];       // lists whose front entries all reach the bound
   uint64_t deep_key[kMaxLists];   // and the key of their last front entry
-  uint64_t T;
   int n_cand;
   int n_deep;
 };
 
 // The k best of the n_cand candidate keys in m.cand, in candidate order, to
-// m.top_s / m.top_i (wave 0), and m.slot_of[rank] = the winner's slot.
+// m.top_s / m.top_i (wave 0), and m.slot_of[rank] = the winner's slot. Up to
+// 128 candidates are ranked directly (two per lane); beyond that a bound
+// that between k and 128 of them reach is found first.
 __device__ __forceinline__ void select_candidates(MergeSmem& m, int nc, int k) {
   const int lane = threadIdx.x & 63;
   uint64_t key[kCandE];
@@ -118,7 +123,7 @@ __device__ __forceinline__ void select_candidates(MergeSmem& m, int nc, int k) {
     const int j = e * kWave + lane;
     key[e] = j < nc ? m.cand[j] : 0ull;
   }
-  const uint64_t T = wave_window_threshold<kCandE>(key, k, kWave);
+  const uint64_t T = wave_window_threshold<kCandE>(key, k, kRankSlots);
   int n = 0;
 #pragma unroll
   for (int e = 0; e < kCandE; ++e) {
@@ -126,18 +131,30 @@ __device__ __forceinline__ void select_candidates(MergeSmem& m, int nc, int k) {
     const unsigned long long mk = __ballot(sel);
     if (sel) {
       const int p = n + lanes_below(mk);
-      if (p < kWave) {
+      if (p < kRankSlots) {
         m.tmp[p] = key[e];
         m.tslot[p] = e * kWave + lane;
       }
     }
     n += __popcll(mk);
   }
-  n = min(n, kWave);
-  pad_keys(m.tmp, n);
-  const int slot = lane < n ? m.tslot[lane] : 0;
-  const int r = wave_rank_emit(m.tmp, n, k, m.top_s, m.top_i);
-  if (lane < n && r < k) m.slot_of[r] = slot;
+  n = min(n, kRankSlots);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {   // zeros up to round_up(n, 8)
+    const int q = lane + h * kWave;
+    if (q >= n && q < ((n + 7) & ~7)) m.tmp[q] = 0ull;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int slot[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) slot[h] = lane + h * kWave < n ? m.tslot[lane + h * kWave] : 0;
+  int r[2];
+  wave_rank_emit2(m.tmp, n, k, m.top_s, m.top_i, r);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (r[h] < k) m.slot_of[r[h]] = slot[h];
 }
 
 // Grid (G, B), 512 threads: block (g, b) merges row b's n lists (sorted,
@@ -145,11 +162,12 @@ __device__ __forceinline__ void select_candidates(MergeSmem& m, int nc, int k) {
 // RESCORE, gives the winners their exact logits. All G blocks of a row
 // compute the same winners; block 0 writes idx and score.
 //  1. The first 4 entries of every list are read in one coalesced pass (one
-//     list per thread) and the heads go to LDS.
-//  2. Wave 0 finds a bound T that between k and k + k/4 + 4 heads reach;
-//     every thread sends its front entries that reach T to the candidate
-//     buffer. Only a list whose 4th entry still reaches T can hold more
-//     candidates; those (rare) lists are read further, one per wave.
+//     list per thread).
+//  2. A bound T that at least k of these front entries reach comes from a
+//     histogram of their score images (below); every thread sends its front
+//     entries that reach T to the candidate buffer. Only a list whose 4th
+//     entry still reaches T can hold more candidates; those (rare) lists are
+//     read further, one per wave.
 //  3. Wave 0 ranks the candidates. Meanwhile, when there are few enough
 //     candidates, waves 1..7 of the G blocks already compute the logits of
 //     all of them, so the W rows are in flight during the selection: a
@@ -169,7 +187,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
   const int G = gridDim.x, g = blockIdx.x;
 
   // 1. the first kFront entries of every list (contiguous across lists in
-  //    the depth-major layout), one list per thread; heads to LDS
+  //    the depth-major layout), one list per thread
   const int64_t R = b * (int64_t)L * n;   // row base
   const int F = min(kFront, L);           // front entries held
   const int p = threadIdx.x;
@@ -183,40 +201,69 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
     fi[j] = part_i[R + (int64_t)jc * n + pc];
     if (p >= n || j >= L) fi[j] = kSentinelId;
   }
-  if (p < n) m.heads[p] = fi[0] != kSentinelId ? cand_key(fs[0], fi[0]) : 0ull;
+  // score images (order-preserving, -0 as +0); 0 marks an empty entry
+  uint32_t fk[kFront];
+#pragma unroll
+  for (int j = 0; j < kFront; ++j) fk[j] = fi[j] != kSentinelId ? order_key(fs[j] + 0.0f) : 0u;
+  {
+    const uint32_t hk = fk[0];
+    const uint32_t wmn = wave_min_u32(hk ? hk : 0xFFFFFFFFu), wmx = wave_max_u32(hk);
+    const int wc = __popcll(__ballot(hk != 0));
+    if (lane == 0) {
+      m.wmin[wave] = wmn;
+      m.wmax[wave] = wmx;
+      m.wcnt[wave] = wc;
+    }
+  }
+  if (threadIdx.x < kHistBins) m.hist[threadIdx.x] = 0;
   if (threadIdx.x == 0) {
     m.n_cand = 0;
     m.n_deep = 0;
   }
   __syncthreads();
 
-  // 2. the bound, then the candidates
-  if (wave == 0) {
-    uint64_t key[kHeadE];
+  // 2. the bound Tk (a score image): with more than k non-empty heads, the
+  //    front entries are counted in 256 bins of images between the lowest
+  //    and the highest head, and Tk is the lower edge of the highest bin at
+  //    which the count from the top reaches k. The edges are images, so the
+  //    count at Tk is exact: at least k entries reach Tk. (Every front entry at
+  //    or above the k-th best head lies in the binned range.) With k heads
+  //    or fewer, Tk = 1 and every non-empty entry counts.
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  int nheads = 0;
 #pragma unroll
-    for (int e = 0; e < kHeadE; ++e) {
-      const int q = e * kWave + lane;
-      key[e] = q < n ? m.heads[q] : 0ull;
-    }
-    const uint64_t T1 = wave_window_threshold<kHeadE>(key, k, min(kWave, k + k / 4 + 4));
-    if (lane == 0) m.T = T1;
+  for (int w = 0; w < kMergeWaves; ++w) {
+    kmin = min(kmin, m.wmin[w]);
+    kmax = max(kmax, m.wmax[w]);
+    nheads += m.wcnt[w];
   }
-  __syncthreads();
-  // The bound as (score, id): key >= T1 holds when the score is larger, or
-  // equal with (unsigned) id <= 0xFFFFFFFF - low word of T1 (every id when
-  // the bound came from the window, whose low word is 0).
-  const uint64_t T1 = m.T;
-  const float ts = key_score(T1);
-  const uint32_t tid = 0xFFFFFFFFu - (uint32_t)T1;
-  const bool all = T1 == 1;   // every non-empty entry counts
-  auto reaches = [&](float sc, int id) {
-    sc = sc + 0.0f;
-    return id != kSentinelId && (all || sc > ts || (sc == ts && (uint32_t)id <= tid));
-  };
+  uint32_t Tk = 1u;
+  if (nheads > k) {
+    const uint32_t R = kmax - kmin;
+    const int shift = R >= (uint32_t)kHistBins ? 24 - __clz(R) : 0;   // R >> shift < 256
+#pragma unroll
+    for (int j = 0; j < kFront; ++j)
+      if (fk[j] >= kmin) atomicAdd(&m.hist[min((fk[j] - kmin) >> shift, (uint32_t)kHistBins - 1)], 1u);
+    __syncthreads();
+    // every wave: counts from the top; lane l holds bins 255 - 4l - i
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = m.hist[kHistBins - 1 - 4 * lane - i] + (i ? c[i - 1] : 0u);
+    const uint32_t above = wave_incl_scan_u32(c[3]) - c[3];   // in lanes before this one
+    const unsigned long long reach = __ballot(above + c[3] >= (uint32_t)k);
+    const int l0 = __builtin_ctzll(reach);   // first lane whose bins reach k (nheads > k: one does)
+    int i0 = 3;
+#pragma unroll
+    for (int i = 2; i >= 0; --i) i0 = above + c[i] >= (uint32_t)k ? i : i0;
+    const int bstar = kHistBins - 1 - 4 * l0 - __builtin_amdgcn_readlane(i0, l0);
+    Tk = kmin + ((uint32_t)bstar << shift);
+  }
+  // An entry counts when its image reaches Tk (empty entries never do).
+  auto reaches = [&](float sc, int id) { return id != kSentinelId && order_key(sc + 0.0f) >= Tk; };
   {
     uint32_t pass = 0;
 #pragma unroll
-    for (int j = 0; j < kFront; ++j) pass |= (reaches(fs[j], fi[j]) ? 1u : 0u) << j;
+    for (int j = 0; j < kFront; ++j) pass |= (fk[j] != 0u && fk[j] >= Tk ? 1u : 0u) << j;
     // slots from a prefix over the wave's lanes of their counts (bit planes)
     const int cnt = __popc(pass);
     int before = 0, wave_total = 0;
@@ -229,7 +276,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
     int base = 0;
     if (wave_total) {
       if (lane == 0) base = atomicAdd(&m.n_cand, wave_total);
-      base = __shfl(base, 0);
+      base = __builtin_amdgcn_readfirstlane(base);
     }
     int slot = base + before;
 #pragma unroll

@@ -32,7 +32,7 @@ template <int NB, int NL>
 __global__ void __launch_bounds__(kSmallThreads) down_small_kernel(const uint16_t* __restrict__ Q,
                                                                    const uint16_t* __restrict__ H, int r,
                                                                    int d, int B, uint16_t* __restrict__ Z) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int j = blockIdx.x * kWavesSmall + wave;
   if (j >= r) return;
   const uint16_t* q = Q + (int64_t)j * d;
@@ -72,7 +72,7 @@ struct SmallLds {
 template <int NB>
 __device__ __forceinline__ void finish_block(SmallLds<NB>& sm, WaveSel<NB>& st, int B, int k,
                                              float* __restrict__ part_s, int* __restrict__ part_i) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int nblk = gridDim.x;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -102,10 +102,10 @@ __device__ __forceinline__ void finish_block(SmallLds<NB>& sm, WaveSel<NB>& st, 
 // KiB of consecutive rows. Block x owns the contiguous slice
 // [V*x/n, V*(x+1)/n) (at most kBlockRows rows) and each wave a quarter of
 // it; the next U wave loads are issued before the current ones are used.
-// The scores go to LDS. After the pass the block copies them to raw[b][v]
-// (coalesced) and wave b writes the L best of the slice for row b, in
-// order, entry j to part_[b][j][x] (depth-major, so that the leading entries
-// of all lists are contiguous for the merge). L is small (min(4, k)): the
+// The scores go to LDS. After the pass wave b writes the L best of the
+// slice for row b, in order, entry j to part_[b][j][x] (depth-major, so that
+// the leading entries of all lists are contiguous for the merge), while the
+// other waves copy the scores to raw[b][v] (coalesced). L is small (min(4, k)): the
 // merge needs more of a slice only when its L-th entry still reaches the
 // merge's bound, and then reads the slice's raw scores.
 constexpr int kBlockRows = 512;
@@ -116,69 +116,90 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
     float* __restrict__ part_s, int* __restrict__ part_i, float* __restrict__ raw) {
   constexpr int LPR = K / 8;
   constexpr int RPL = kWave / LPR;
-  constexpr int U = 8;
+  constexpr int U = 8;   // wave loads per group
   constexpr int STEP = U * RPL;
   static_assert(K % 8 == 0 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "row length");
   __shared__ float sc[NB][E * kWave];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int c = lane % LPR, sub = lane / LPR;
 
+  // z first (one load per row, unpredicated), widened only after the first
+  // group of P loads is issued
+  u32x4 zr[NB];
   f32x8 zc[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) zc[b] = widen8(b < B ? load16(X + (int64_t)b * K + 8 * c) : u32x4{0u, 0u, 0u, 0u});
+  for (int b = 0; b < NB; ++b) zr[b] = load16(X + (int64_t)(b < B ? b : 0) * K + 8 * c);
 
+  // slice bounds V*x/n in 32 bits: this path keeps V*n below 2^27
   const int64_t nblk = gridDim.x;
-  const int64_t blo = V * blockIdx.x / nblk, bhi = V * (blockIdx.x + 1) / nblk;
+  const uint32_t v32 = (uint32_t)V, n32 = gridDim.x;
+  const int64_t blo = v32 * blockIdx.x / n32, bhi = v32 * (blockIdx.x + 1) / n32;
   const int64_t wlo = blo + (bhi - blo) * wave / kWavesSmall;
   const int64_t whi = blo + (bhi - blo) * (wave + 1) / kWavesSmall;
 
-  // Rows past the wave's range are loaded from its last row (a valid
-  // address, so no load is predicated) and never kept.
-  const int64_t last = whi - 1;
-  u32x4 cur[U], nxt[U];
-  if (wlo < whi) {
+  // The wave's rows go in groups of STEP (U wave loads), two groups in
+  // flight: group g + 1 is issued before group g is used. The groups are
+  // unrolled with fixed buffers (no register copies, which would wait for
+  // the loads in flight), and the last group prefetches nothing, so no load
+  // is outstanding after the pass. Rows past the wave's range are loaded
+  // from its last row (a valid address, so no load is predicated) and never
+  // kept (a wave without rows loads row 0).
+  constexpr int NGM = (E * kWave / kWavesSmall + STEP - 1) / STEP;   // most groups of a wave
+  const int64_t last = whi > 0 ? whi - 1 : 0;
+  const int ng = wlo < whi ? (int)((whi - wlo + STEP - 1) / STEP) : 0;
+  u32x4 buf[2][U];
+  auto issue = [&](int q, int64_t base) {
 #pragma unroll
     for (int t = 0; t < U; ++t) {
-      const int64_t row = wlo + t * RPL + sub;
-      cur[t] = load16(M + (row < last ? row : last) * K + 8 * c);
+      const int64_t row = base + t * RPL + sub;
+      buf[q][t] = load16(M + (row < last ? row : last) * K + 8 * c);
     }
-  }
-  for (int64_t base = wlo; base < whi; base += STEP) {
-#pragma unroll
-    for (int t = 0; t < U; ++t) {
-      const int64_t row = base + STEP + t * RPL + sub;
-      nxt[t] = load16(M + (row < last ? row : last) * K + 8 * c);
-    }
+  };
+  auto consume = [&](int q, int64_t base) {
 #pragma unroll
     for (int t = 0; t < U; ++t) {
       const int64_t row = base + t * RPL + sub;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         if (b >= B) break;
-        const float s = group_sum<LPR>(dot8_bf16(cur[t], zc[b], 0.f));
+        const float s = group_sum<LPR>(dot8_bf16(buf[q][t], zc[b], 0.f));
         if (c == 0 && row < whi) sc[b][row - blo] = s;
       }
     }
+  };
+  issue(0, wlo);   // unconditional: a branch here would make the first use wait for every load
+  __builtin_amdgcn_sched_barrier(0);   // all of them before anything waits for z
 #pragma unroll
-    for (int t = 0; t < U; ++t) cur[t] = nxt[t];
+  for (int b = 0; b < NB; ++b) zc[b] = widen8(b < B ? zr[b] : u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+  for (int g = 0; g < NGM; ++g) {
+    const int64_t base = wlo + (int64_t)g * STEP;
+    if (g + 1 < ng) {
+      issue((g + 1) & 1, base + STEP);
+      consume(g & 1, base);
+    } else {
+      if (g < ng) consume(g & 1, base);
+      break;
+    }
   }
   __syncthreads();
   const int nrows = (int)(bhi - blo);
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    if (b >= B) break;
-    for (int j = threadIdx.x; j < nrows; j += kSmallThreads) raw[(int64_t)b * V + blo + j] = sc[b][j];
-  }
   if (wave < B) {
-    const int b = wave;
-    uint64_t key[E];
+    const int64_t o = (int64_t)wave * L * nblk + blockIdx.x;
+    wave_top_few<E>(sc[wave], nrows, (int)blo, L, part_s + o, part_i + o, nblk);
+  }
+  // The raw scores: the waves without a row copy all rows; when every wave
+  // has a row (B = 4), each copies its own after its selection.
+  const int idle = kWavesSmall - B;
+  const int t0 = idle > 0 ? (wave - B) * kWave + lane : lane;
+  const int step = idle > 0 ? idle * kWave : kWave;
+  if (idle == 0 || wave >= B) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = e * kWave + lane;
-      key[e] = j < nrows ? cand_key(sc[b][j], (int)(blo + j)) : 0ull;
+    for (int b = 0; b < NB; ++b) {
+      if (b >= B) break;
+      if (idle == 0 && b != wave) continue;
+      for (int j = t0; j < nrows; j += step) raw[(int64_t)b * V + blo + j] = sc[b][j];
     }
-    const int64_t o = (int64_t)b * L * nblk + blockIdx.x;
-    wave_top_argmax<E>(key, L, part_s + o, part_i + o, nblk);
   }
 }
 
@@ -192,7 +213,7 @@ __global__ void __launch_bounds__(kSmallThreads) select_long_kernel(
     float* __restrict__ part_s, int* __restrict__ part_i) {
   __shared__ SmallLds<NB> sm;
   __shared__ u32x4 xs[NB][NL * kWave];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   for (int e = threadIdx.x; e < NB * NL * kWave; e += kSmallThreads) {
     const int b = e / (NL * kWave), rem = e - b * NL * kWave;
     const int col = rem * 8;
@@ -200,8 +221,9 @@ __global__ void __launch_bounds__(kSmallThreads) select_long_kernel(
   }
   __syncthreads();
 
-  const int64_t nblk = gridDim.x;
-  const int64_t blo = V * blockIdx.x / nblk, bhi = V * (blockIdx.x + 1) / nblk;
+  // slice bounds V*x/n in 32 bits: this path keeps V*n below 2^27
+  const uint32_t v32 = (uint32_t)V, n32 = gridDim.x;
+  const int64_t blo = v32 * blockIdx.x / n32, bhi = v32 * (blockIdx.x + 1) / n32;
   const int64_t wlo = blo + (bhi - blo) * wave / kWavesSmall;
   const int64_t whi = blo + (bhi - blo) * (wave + 1) / kWavesSmall;
   const int64_t last = whi - 1;
@@ -320,6 +342,7 @@ static hipError_t launch_short_k(const void* M, const void* X, int64_t V, int64_
   dim3 grid(nblk);
   const int64_t rows = (V + nblk - 1) / nblk;   // most rows of one block
   const int L = small_list_len(k);
+  if (rows > 8 * kWave || V * nblk >= (int64_t)1 << 32) return hipErrorInvalidValue;
   if (rows <= 4 * kWave) {
     LRH_NB_DISPATCH(B, LRH_LAUNCH(t, (select_short_kernel<K, NB, 4>), grid, dim3(kSmallThreads), 0, stream,
                                   (const uint16_t*)M, (const uint16_t*)X, V, (int)B, L, ps, pi, raw));
@@ -349,6 +372,7 @@ hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, i
 
 hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* ps,
                               int* pi, hipStream_t stream, Timing t) {
+  if (V > (int64_t)kMaxSmallBlocks * kBlockRows) return hipErrorInvalidValue;
   dim3 grid(small_blocks(V));
   const int nl = row_loads(K);
   LRH_NB_DISPATCH(B, LRH_NL_DISPATCH(nl, LRH_LAUNCH(t, (select_long_kernel<NB, NL>), grid, dim3(kSmallThreads), 0,

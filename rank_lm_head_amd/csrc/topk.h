@@ -19,8 +19,8 @@
 //  * wave_select_threshold: the exact k-th best by a full bisection, used
 //    when ties keep the window from being reached.
 //
-//  * wave_top_argmax: the few best (a slice's leading entries) by repeated
-//    wave-wide argmax.
+//  * wave_top_few: the few best (a slice's leading entries) by repeated
+//    wave-wide maxima of 32-bit score images.
 //
 //  * merge_lists_seq: a wave-wide fold of sorted lists, the fallback of the
 //    merge kernel when too many entries tie at its threshold.
@@ -130,6 +130,26 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
   x = max(x, dpp_u32<0x141>(x));
   x = max(x, dpp_u32<0x140>(x));
   return max(max(rl(x, 0), rl(x, 16)), max(rl(x, 32), rl(x, 48)));
+}
+
+// Inclusive prefix sum over the lanes of a wave (lane order): DPP row shifts
+// by 1, 2, 4 and 8 inside each row of 16 lanes (lanes whose source falls
+// outside the row add 0), then the totals of the rows below by readlane.
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp_shr_or_0(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, Ctrl, 0xf, 0xf, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  x += dpp_shr_or_0<0x111>(x);
+  x += dpp_shr_or_0<0x112>(x);
+  x += dpp_shr_or_0<0x114>(x);
+  x += dpp_shr_or_0<0x118>(x);
+  const int row = (threadIdx.x & 63) >> 4;
+  const uint32_t r0 = rl(x, 15), r1 = rl(x, 31), r2 = rl(x, 47);
+  x += row >= 1 ? r0 : 0u;
+  x += row >= 2 ? r1 : 0u;
+  x += row >= 3 ? r2 : 0u;
+  return x;
 }
 
 // Wave-wide exact selection threshold over E keys per lane: returns T such
@@ -332,6 +352,47 @@ __device__ __forceinline__ void pad_keys(uint64_t* tmp, int n) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// As wave_rank_emit for n <= 128 distinct keys, two per lane (tmp[lane] and
+// tmp[lane + 64]); tmp[n .. round_up(n, 8)) must hold zeros. The ranks of
+// the lane's two keys go to r[0], r[1] (k or more: no winner); k <= 64.
+__device__ __forceinline__ void wave_rank_emit2(const uint64_t* tmp, int n, int k, float* __restrict__ out_s,
+                                                int* __restrict__ out_i, int (&r)[2]) {
+  const int lane = threadIdx.x & 63;
+  uint64_t mine[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) mine[h] = lane + h * kWave < n ? tmp[lane + h * kWave] : 0ull;
+  const u64x2* t2 = reinterpret_cast<const u64x2*>(tmp);
+  r[0] = r[1] = 0;
+  for (int t = 0; t < n; t += 16) {
+    u64x2 a[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = t2[t / 2 + q];
+    const int qn = t + 8 < n ? 8 : 4;   // past round_up(n, 8) the slots may be stale
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (q < qn) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) r[h] += (a[q].x > mine[h]) + (a[q].y > mine[h]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (lane + h * kWave < n) {
+      if (r[h] < k) {
+        out_s[r[h]] = key_score(mine[h]);
+        out_i[r[h]] = key_id(mine[h]);
+      }
+    } else {
+      r[h] = k;
+    }
+  }
+  if (lane >= n && lane < k) {   // fewer than k keys: empty ranks n .. k-1
+    out_s[lane] = neg_inf();
+    out_i[lane] = kSentinelId;
+  }
+}
+
 // The k best of E keys per lane (distinct where non-empty), in candidate
 // order, to out_s/out_i[r * stride] (r = 0 .. k-1); `tmp` is 64 words of
 // LDS owned by the wave.
@@ -359,47 +420,54 @@ __device__ __forceinline__ void wave_topk_emit(const uint64_t (&key)[E], int k, 
 // ------------------------------------------------- a few best by argmax
 // Wave-wide maximum of a 64-bit key: DPP inside rows of 16 lanes, then the
 // four row results by readlane.
-template <int Ctrl>
-__device__ __forceinline__ void dpp_max_step(uint32_t& hi, uint32_t& lo) {
-  const uint32_t oh = dpp_u32<Ctrl>(hi), ol = dpp_u32<Ctrl>(lo);
-  const bool take = ((uint64_t)oh << 32 | ol) > ((uint64_t)hi << 32 | lo);
-  hi = take ? oh : hi;
-  lo = take ? ol : lo;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-  uint32_t hi = (uint32_t)(x >> 32), lo = (uint32_t)x;
-  dpp_max_step<0xB1>(hi, lo);
-  dpp_max_step<0x4E>(hi, lo);
-  dpp_max_step<0x141>(hi, lo);
-  dpp_max_step<0x140>(hi, lo);
-  uint64_t m = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t v = ((uint64_t)rl(hi, 16 * r) << 32) | rl(lo, 16 * r);
-    m = v > m ? v : m;
-  }
-  return m;
-}
-
-// The L best of E keys per lane (distinct where non-empty; L small), in
-// candidate order, to out_s/out_i[r * stride], r = 0 .. L-1, by L rounds of
-// a wave-wide argmax (the winning key is cleared each round). Empty ranks get
-// empty entries. The keys are consumed.
+// The L best (L <= 64) of a slice's n <= E * 64 scores held in LDS (entry j
+// at sc[j], token id id0 + j), in candidate order, to out_s/out_i[r * stride]
+// for r < L; ranks past n get empty entries. Entry j = e * 64 + lane sits in
+// lane `lane` as element e, so within a lane a lower e is a lower id.
+// Each round takes the wave-wide maximum of the 32-bit score images (each
+// lane offers its best element, the lowest e among equal ones), then the
+// lanes holding it: almost always one, and otherwise the lowest id among
+// them (smallest e, then lowest lane). The winner's element is cleared.
 template <int E>
-__device__ __forceinline__ void wave_top_argmax(uint64_t (&key)[E], int L, float* __restrict__ out_s,
-                                                int* __restrict__ out_i, int64_t stride) {
+__device__ __forceinline__ void wave_top_few(const float* sc, int n, int id0, int L, float* __restrict__ out_s,
+                                             int* __restrict__ out_i, int64_t stride) {
   const int lane = threadIdx.x & 63;
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = sc[min(e * kWave + lane, n - 1)];
+  uint32_t h[E];   // 0 = empty (no finite score maps to 0)
+#pragma unroll
+  for (int e = 0; e < E; ++e) h[e] = e * kWave + lane < n ? order_key(v[e] + 0.0f) : 0u;
+  float my_s = neg_inf();
+  int my_i = kSentinelId;
   for (int r = 0; r < L; ++r) {
-    uint64_t best = 0;
+    uint32_t best = h[0];
+    int be = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) best = key[e] > best ? key[e] : best;
-    const uint64_t w = wave_max_u64(best);
-#pragma unroll
-    for (int e = 0; e < E; ++e) key[e] = key[e] == w ? 0ull : key[e];
-    if (lane == 0) {
-      out_s[r * stride] = w ? key_score(w) : neg_inf();
-      out_i[r * stride] = w ? key_id(w) : kSentinelId;
+    for (int e = 1; e < E; ++e) {
+      const bool t = h[e] > best;
+      best = t ? h[e] : best;
+      be = t ? e : be;
     }
+    const uint32_t M = wave_max_u32(best);
+    if (M == 0) break;   // fewer than L entries
+    unsigned long long mk = __ballot(best == M);
+    if (mk & (mk - 1)) {   // equal scores in several lanes
+      const uint32_t me = wave_min_u32(best == M ? (uint32_t)be : 0xFFu);
+      mk = __ballot(best == M && (uint32_t)be == me);
+    }
+    const int wl = __builtin_ctzll(mk);
+    const int we = __builtin_amdgcn_readlane(be, wl);
+#pragma unroll
+    for (int e = 0; e < E; ++e) h[e] = (lane == wl && e == we) ? 0u : h[e];
+    if (lane == r) {
+      my_s = __uint_as_float(order_key_inv(M));
+      my_i = id0 + we * kWave + wl;
+    }
+  }
+  if (lane < L) {
+    out_s[lane * stride] = my_s;
+    out_i[lane * stride] = my_i;
   }
 }
 

@@ -285,6 +285,36 @@ def test_duplicate_rows_tie_to_the_lower_id():
     assert len(set(np_(flog)[0].tolist())) == 1
 
 
+@pytest.mark.parametrize("B", [1, 4])
+def test_ties_inside_one_slice_go_to_the_lower_ids(B):
+    """Bitwise copies of the best low-rank row inside one vocabulary slice, at
+    ids that share a lane and ids in different lanes: every tied copy must come
+    out in id order. With five tied entries the slice's 4-entry list is full at
+    the bound, so the merge also reads that slice's raw scores."""
+    V, k = 3000, 6
+    inp = gen.make_custom(V, 128, 32, B, "bf16", seed=12)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=k)
+    tok = int(np_(head.candidates(t["H"][:1], 1)[0])[0, 0])
+    # V = 3000 gives 12 slices of 250 rows; slice 1 is ids [250, 500): ids
+    # 253, 256, 320 and 380 sit in lanes 3, 6, 6, 2 as elements 0, 0, 1, 2
+    dups = [x for x in (253, 256, 320, 380, 441) if x != tok][:4]
+    inp2 = dict(inp)
+    inp2["P"] = inp["P"].copy()
+    for dst in dups:
+        inp2["P"][dst] = inp["P"][tok]
+    P2 = dev(inp2["P"], DEV)
+    h2 = lr.Head(t["Q"], P2, t["W"], B_max=B, k_max=k)
+    idx, score, lg = h2.draft(t["H"], k)
+    torch.cuda.synchronize()
+    tied = sorted(dups + [tok])
+    got = np_(idx)[0].tolist()
+    assert got[:5] == tied, (got, tied)
+    assert len(set(np_(score)[0, :5].tolist())) == 1
+    errs, _ = check_lowrank(inp2, k, np_(idx), np_(score), np_(lg))
+    assert not errs, errs[:5]
+
+
 def test_repeat_calls_and_poisoned_workspace_are_bitwise_stable():
     inp = gen.make_custom(20000, 512, 128, 40, "bf16", seed=6)
     t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
