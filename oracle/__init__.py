@@ -9,6 +9,7 @@ from .lowrank_head import (  # noqa: F401
     vocab_scores, topk_order, selection_stats, exact_logits, lowrank_head,
     full_head,
 )
+from .branching import draft_distribution, branch_order, branches  # noqa: F401
 from .compare import (  # noqa: F401
     check_candidates, check_logits, check_scores, band_counts, ulp_bf16,
     z_step_allowance, LOGIT_RTOL, SCORE_TOL,

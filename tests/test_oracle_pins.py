@@ -394,3 +394,63 @@ def test_golden_snapshot_of_tiny_config():
     assert np.allclose(lr["score"], snap["lowrank_score"], rtol=1e-15, atol=0)
     assert fh["idx"].tolist() == snap["full_idx"]
     assert np.allclose(fh["logits"], snap["full_logits"], rtol=1e-15, atol=0)
+
+
+# ------------------------------------------- draft distribution (D1-D3)
+
+def test_distribution_uniform_logits_give_one_over_k_and_id_order():
+    """Equal logits: every probability is 1/k and the branches come in token-id order."""
+    k = 7
+    ids = np.array([[40, 3, 17, 9, 100, 5, 66]])
+    p, bi, bp, bpath = oracle.branches(np.full((1, k), 2.5), ids, 3, parent=np.array([0.5]))
+    assert np.allclose(p, 1.0 / k, rtol=0, atol=1e-15)
+    assert bi[0].tolist() == [3, 5, 9]
+    assert np.allclose(bp, 1.0 / k) and np.allclose(bpath, 0.5 / k)
+
+
+def test_distribution_of_log_weights_is_the_normalised_weights():
+    """Logits log(w_j): p_j = w_j / sum(w) exactly (closed form of the softmax)."""
+    w = np.array([1.0, 2.0, 3.0, 4.0, 10.0])
+    ids = np.array([[11, 12, 13, 14, 15]])
+    p, bi, bp, _ = oracle.branches(np.log(w)[None, :], ids, 2)
+    assert np.allclose(p[0], w / w.sum(), rtol=1e-14, atol=0)
+    assert bi[0].tolist() == [15, 14]
+    assert np.allclose(bp[0], [10 / 20, 4 / 20], rtol=1e-14)
+
+
+def test_distribution_is_shift_invariant_and_sums_to_one():
+    rng = np.random.default_rng(3)
+    l = rng.normal(size=(5, 32)) * 3
+    ids = np.tile(np.arange(32), (5, 1))
+    p1 = oracle.draft_distribution(l)
+    p2 = oracle.draft_distribution(l + 1000.0)   # large shift: only the max-subtracted form survives it
+    assert np.allclose(p1, p2, rtol=1e-12, atol=1e-300)
+    assert np.allclose(p1.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    # nb = k orders every candidate by probability
+    _, bi, bp, _ = oracle.branches(l, ids, 32)
+    assert all(np.all(np.diff(bp[b]) <= 0) for b in range(5))
+    assert all(sorted(bi[b].tolist()) == list(range(32)) for b in range(5))
+    # nb = 1 is the argmax (first maximum)
+    _, b1, _, _ = oracle.branches(l, ids, 1)
+    assert b1[:, 0].tolist() == np.argmax(l, axis=1).tolist()
+
+
+def test_distribution_empty_slots_get_nothing():
+    """NaN logits (empty candidate slots) get probability 0 and are never branches."""
+    l = np.array([[0.0, np.nan, np.log(3.0), np.nan]])
+    ids = np.array([[7, 0x7FFFFFFF, 9, 0x7FFFFFFF]])
+    p, bi, bp, _ = oracle.branches(l, ids, 4)
+    assert np.allclose(p[0], [0.25, 0.0, 0.75, 0.0], rtol=1e-15, atol=0)
+    assert bi[0].tolist() == [9, 7, -1, -1] and bp[0].tolist() == [0.75, 0.25, 0.0, 0.0]
+
+
+def test_distribution_against_a_plain_loop():
+    """D1 written out element by element with math.exp and math.fsum."""
+    rng = np.random.default_rng(4)
+    l = rng.normal(size=(3, 9))
+    p = oracle.draft_distribution(l)
+    for b in range(3):
+        m = max(l[b])
+        e = [math.exp(x - m) for x in l[b]]
+        s = math.fsum(e)
+        assert np.allclose(p[b], [x / s for x in e], rtol=1e-15, atol=0)
