@@ -149,6 +149,31 @@ int lrhead_draft(lrhead_t h, const void* H, int64_t B, int k,
                  int32_t* idx, float* score, float* logits, void* stream);
 
 /*
+ * The draft distribution over each node's candidates and the node's branches
+ * ("EAGLE-4: One Flexible Drafter for All Batch Sizes and Hardware":
+ * section "Retrieve vocabulary candidates cheaply, then score them exactly",
+ * the probabilities come from the exact logits; section "Why a draft tree
+ * needs a cost model", products of draft probabilities estimate the benefit.
+ * "EAGLE-4 Triples Qwen3 Inference Speed by Adapting to Serving Load",
+ * section "Runtime-sized speculation": one branch per node drafts a chain,
+ * more a tree). For each of the B rows of `logits` / `idx` (device, B x k
+ * row-major, as written by lrhead_draft):
+ *   probs[b, j] = exp(l_j - m) / sum_i exp(l_i - m), over the row's k
+ *   candidates only (the full-vocabulary normaliser would need all V
+ *   logits); NaN logits mark empty slots and get 0;
+ *   br_idx[b, r], br_prob[b, r] (r < nb): the nb most probable candidates in
+ *   order, equal probabilities going to the lower token id; slots past the
+ *   existing candidates hold -1 and 0;
+ *   br_path[b, r] = parent[b] * br_prob[b, r] (parent may be NULL: 1).
+ * Requirements: 1 <= nb <= k <= 64, B >= 0, device pointers, outputs
+ * B x k (probs) and B x nb (the rest), fp32 / int32. Needs no handle and no
+ * workspace; asynchronous on `stream`.
+ */
+int lrhead_branch(const float* logits, const int32_t* idx, const float* parent,
+                  int64_t B, int k, int nb, float* probs, int32_t* br_idx,
+                  float* br_prob, float* br_path, void* stream);
+
+/*
  * Profiling aid: hipEvent_t handles (passed as void*) that later calls on
  * this handle attach to the dispatch of the vocabulary score pass
  * (lrhead_candidates, lrhead_draft, fullhead_topk; for row batches its main

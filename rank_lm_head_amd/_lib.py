@@ -28,6 +28,7 @@ SIGNATURES = {
     "fullhead_logits": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, ctypes.c_int, _vp, _vp]),
     "fullhead_topk": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp, _vp, _vp]),
     "lrhead_draft": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp, _vp, _vp, _vp]),
+    "lrhead_branch": (ctypes.c_int, [_vp, _vp, _vp, _c_i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]),
     "lrhead_set_stage_events": (ctypes.c_int, [_vp, _vp, _vp]),
     "lrhead_destroy": (None, [_vp]),
     "lrhead_strerror": (ctypes.c_char_p, [ctypes.c_int]),

@@ -111,6 +111,12 @@ hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n
                         int64_t V, int64_t B, int k, const void* W, const void* H, int d, int32_t* idx,
                         float* score, float* logits, hipStream_t stream);
 
+// ---------------------------------------------------- kernels_branch.hip
+// Softmax of each row's k candidate logits, the nb most probable as
+// branches (ties to the lower id) and their path probabilities.
+hipError_t launch_branch(const float* logits, const int32_t* idx, const float* parent, int64_t B, int k, int nb,
+                         float* probs, int32_t* br_idx, float* br_prob, float* br_path, hipStream_t stream);
+
 // logits[b, j] = W[idx[b, j], :] . h_b (NaN for ids outside [0, V)).
 hipError_t launch_rescore(int dtype, const void* W, const void* H, const int32_t* idx, int64_t B,
                           int k, int64_t V, int d, float* logits, hipStream_t stream);

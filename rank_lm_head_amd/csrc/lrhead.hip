@@ -309,6 +309,20 @@ int lrhead_draft(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, floa
   return enqueue_head(h, H, B, k, idx, score, logits, static_cast<hipStream_t>(stream));
 }
 
+int lrhead_branch(const float* logits, const int32_t* idx, const float* parent, int64_t B, int k, int nb,
+                  float* probs, int32_t* br_idx, float* br_prob, float* br_path, void* stream) {
+  if (B < 0) return fail(LRHEAD_ERANGE, "B = %lld is negative", (long long)B);
+  if (k < 1 || k > LRHEAD_K_MAX) return fail(LRHEAD_ERANGE, "k = %d outside [1, %d]", k, LRHEAD_K_MAX);
+  if (nb < 1 || nb > k) return fail(LRHEAD_ERANGE, "nb = %d outside [1, k = %d]", nb, k);
+  if (B == 0) return LRHEAD_OK;
+  if (!logits || !idx || !probs || !br_idx || !br_prob || !br_path)
+    return fail(LRHEAD_EINVAL, "logits, idx, probs, br_idx, br_prob and br_path must be non-NULL");
+  LRH_HIP(lrh::launch_branch(logits, idx, parent, B, k, nb, probs, br_idx, br_prob, br_path,
+                             static_cast<hipStream_t>(stream)),
+          "branch launch");
+  return LRHEAD_OK;
+}
+
 int lrhead_set_stage_events(lrhead_t h, void* before, void* after) {
   LRH_TRY(check_handle(h));
   if ((before == nullptr) != (after == nullptr))

@@ -147,3 +147,31 @@ class Head:
             self.close()
         except Exception:
             pass
+
+
+def branch(logits: torch.Tensor, idx: torch.Tensor, nb: int, parent: torch.Tensor | None = None):
+    """Draft distribution over each row's candidates and its nb branches.
+
+    logits: [B, k] float32, idx: [B, k] int32 (as returned by Head.draft),
+    parent: optional [B] float32 path probabilities. Returns (probs [B, k],
+    branch ids [B, nb], branch probabilities [B, nb], branch path
+    probabilities [B, nb]); see lrhead_branch in include/lrhead.h.
+    """
+    _need(logits.is_cuda and idx.is_cuda, "logits and idx must be device tensors")
+    _need(logits.dtype == torch.float32 and idx.dtype == torch.int32, "logits float32, idx int32")
+    _need(logits.dim() == 2 and idx.shape == logits.shape, "logits and idx must be [B, k] alike")
+    _need(logits.is_contiguous() and idx.is_contiguous(), "logits and idx must be contiguous")
+    B, k = logits.shape
+    if parent is not None:
+        _need(parent.is_cuda and parent.dtype == torch.float32 and parent.shape == (B,) and parent.is_contiguous(),
+              "parent must be a contiguous float32 device tensor of shape [B]")
+    lib = _lib.load()
+    dev = logits.device
+    probs = torch.empty((B, k), dtype=torch.float32, device=dev)
+    br_idx = torch.empty((B, nb), dtype=torch.int32, device=dev)
+    br_prob = torch.empty((B, nb), dtype=torch.float32, device=dev)
+    br_path = torch.empty((B, nb), dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    _lib.check(lib.lrhead_branch(_ptr(logits), _ptr(idx), _ptr(parent), B, k, nb, _ptr(probs), _ptr(br_idx),
+                                 _ptr(br_prob), _ptr(br_path), stream), "lrhead_branch")
+    return probs, br_idx, br_prob, br_path

@@ -86,6 +86,19 @@ def test_calls_reject_null_handle():
     lib.lrhead_destroy(None)        # a no-op
 
 
+def test_branch_rejects_bad_arguments_before_hip():
+    lib = _lib.load()
+    p = ctypes.c_void_p(0x20000)
+    args = lambda B, k, nb, ptr=p: (ptr, ptr, None, B, k, nb, ptr, ptr, ptr, ptr, None)
+    assert lib.lrhead_branch(*args(1, 0, 1)) == _lib.ERANGE       # k < 1
+    assert lib.lrhead_branch(*args(1, 65, 1)) == _lib.ERANGE      # k > 64
+    assert lib.lrhead_branch(*args(1, 8, 9)) == _lib.ERANGE       # nb > k
+    assert lib.lrhead_branch(*args(1, 8, 0)) == _lib.ERANGE
+    assert lib.lrhead_branch(*args(-1, 8, 2)) == _lib.ERANGE
+    assert lib.lrhead_branch(*args(1, 8, 2, None)) == _lib.EINVAL
+    assert lib.lrhead_branch(*args(0, 8, 2, None)) == _lib.OK      # B == 0 enqueues nothing
+
+
 def test_strerror_covers_every_code():
     lib = _lib.load()
     for code in (0, -1, -2, -3, -4, -5, -6, -7):

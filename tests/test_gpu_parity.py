@@ -328,3 +328,64 @@ def test_repeat_calls_and_poisoned_workspace_are_bitwise_stable():
     f1 = [np_(x) for x in head.full_topk(t["H"], 64)]
     f2 = [np_(x) for x in head.full_topk(t["H"], 64)]
     assert all(np.array_equal(a, b) for a, b in zip(f1, f2))
+
+
+# ------------------------------------------- draft distribution (D1-D3)
+
+def check_branch(logits, idx, nb, parent, probs, br_i, br_p, br_path):
+    """Device branch outputs against oracle D1-D3 on the device's own logits:
+    probabilities within 1e-5 relative (fp32 exp and sum against float64),
+    branch ids equal up to neighbours whose probabilities are within 1e-6."""
+    p_ref, bi_ref, bp_ref, bpath_ref = oracle.branches(logits, idx, nb, parent)
+    errs = []
+    if not np.allclose(probs, p_ref, rtol=1e-5, atol=1e-7):
+        errs.append(f"probs off by {np.max(np.abs(probs - p_ref)):.3g}")
+    for b in range(logits.shape[0]):
+        got, want = br_i[b].tolist(), bi_ref[b].tolist()
+        if got != want:
+            pm = {int(i): float(p_ref[b][j]) for j, i in enumerate(idx[b]) if not np.isnan(logits[b, j])}
+            for r, (g, w) in enumerate(zip(got, want)):
+                if g != w and not (g in pm and w in pm and abs(pm[g] - pm[w]) <= 1e-6 * max(pm[w], 1e-30)):
+                    errs.append(f"row {b} rank {r}: id {g}, oracle {w}")
+        if not np.allclose(br_p[b], bp_ref[b], rtol=1e-5, atol=1e-7):
+            errs.append(f"row {b}: branch probabilities")
+        if not np.allclose(br_path[b], bpath_ref[b], rtol=1e-5, atol=1e-7):
+            errs.append(f"row {b}: path probabilities")
+    return errs
+
+
+def test_branch_after_a_draft_call_matches_the_oracle():
+    """Draft distribution on the candidates of a real draft call (batch-1 and a
+    64-node tree), nb = 1 (a chain), 4 and k, with parent path probabilities."""
+    for cid in (2, 4):
+        inp, t = config(cid)
+        cfg = inp["cfg"]
+        head = head_for(inp, t)
+        idx, _, lg = head.draft(t["H"], cfg.k)
+        parent = torch.rand(cfg.B, device=DEV, generator=torch.Generator(DEV).manual_seed(cid))
+        for nb in (1, 4, cfg.k):
+            say(f"[run] branch c{cid} nb={nb}")
+            out = lr.branch(lg, idx, nb, parent)
+            torch.cuda.synchronize()
+            errs = check_branch(np_(lg), np_(idx), nb, np_(parent), *[np_(x) for x in out])
+            assert not errs, errs[:5]
+
+
+def test_branch_edge_cases():
+    """Equal logits (ties to the lower id), empty slots (NaN), k = 1, large shifts."""
+    rng = np.random.default_rng(5)
+    B, k = 6, 64
+    l = rng.normal(size=(B, k)).astype(np.float32) * 4
+    l[0] = 1.25                                   # all tied
+    l[1, 40:] = np.nan                            # fewer candidates than branches below
+    l[2] += 80.0                                  # exp overflows without the max subtraction
+    l[3, ::3] = l[3, 0]                           # many ties with the row's first logit
+    ids = np.stack([rng.permutation(100000)[:k] for _ in range(B)]).astype(np.int32)
+    ids[1, 40:] = 0x7FFFFFFF
+    for nb in (1, 5, 48, 64):
+        out = lr.branch(torch.from_numpy(l).to(DEV), torch.from_numpy(ids).to(DEV), nb)
+        torch.cuda.synchronize()
+        errs = check_branch(l, ids, nb, None, *[np_(x) for x in out])
+        assert not errs, (nb, errs[:5])
+    one = lr.branch(torch.tensor([[3.0]], device=DEV), torch.tensor([[17]], dtype=torch.int32, device=DEV), 1)
+    assert np_(one[0]).tolist() == [[1.0]] and np_(one[1]).tolist() == [[17]]
