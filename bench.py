@@ -59,6 +59,12 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB with a plain device copy, so "
                          "that hardware byte counters can be scaled against a known size")
+    ap.add_argument("--table", action="store_true",
+                    help="instead of the headline: a latency table of the draft-head call over "
+                         "B x r x k (and of the full-head baseline over B x k), one JSON object")
+    ap.add_argument("--recall", action="store_true",
+                    help="instead of the headline: recall of the full head's top-b inside the "
+                         "low-rank top-k for r in 128/256/512, one JSON object")
     return ap.parse_args()
 
 
@@ -188,6 +194,105 @@ def cpu_baseline(inp: dict, seconds: float) -> dict:
             "us_per_call": el / n * 1e6}
 
 
+# ------------------------------------------------ latency table and recall
+# Synthetic heads for the sweeps, generated on the device with torch's
+# seeded generator in the recipe of the workloads: Q, P and E with standard
+# deviation 1/sqrt(d), W = P.Q + 0.1 E rounded once to bf16, hidden rows
+# RMS-normalised. (The headline and the parity tests use the numpy
+# generator of gen/; the sweeps need many shapes quickly.)
+TABLE_V, TABLE_D = 151936, 5120
+TABLE_B = (1, 8, 64, 256, 2048)
+TABLE_R = (128, 256, 512)
+TABLE_K = (8, 32, 64)
+
+
+def synthetic_head(torch, dev, V, d, r, seed, with_w=True):
+    g = torch.Generator(device=dev).manual_seed(seed)
+    sd = 1.0 / math.sqrt(d)
+    Q = (torch.randn(r, d, generator=g, device=dev) * sd).to(torch.bfloat16)
+    P = (torch.randn(V, r, generator=g, device=dev) * sd).to(torch.bfloat16)
+    if not with_w:
+        return Q, P, None
+    W = torch.empty(V, d, dtype=torch.bfloat16, device=dev)
+    Qf = Q.float()
+    for c0 in range(0, V, 16384):
+        c1 = min(V, c0 + 16384)
+        E = torch.randn(c1 - c0, d, generator=g, device=dev) * sd
+        W[c0:c1] = (P[c0:c1].float() @ Qf + 0.1 * E).to(torch.bfloat16)
+    return Q, P, W
+
+
+def synthetic_rows(torch, dev, B, d, seed):
+    g = torch.Generator(device=dev).manual_seed(seed)
+    h = torch.randn(B, d, generator=g, device=dev)
+    return (h / h.pow(2).mean(dim=1, keepdim=True).sqrt()).to(torch.bfloat16)
+
+
+def latency_table(torch, lr, dev, steps: int) -> dict:
+    """Draft-head call latency (cache-cold graph replay, as the headline) for
+    every (B, r, k) of the grid, and the full-head baseline for every (B, k)."""
+    rows, full = [], []
+    for r in TABLE_R:
+        Q0, P0, W = synthetic_head(torch, dev, TABLE_V, TABLE_D, r, seed=7000 + r)
+        R = max(1, math.ceil(2 * MALL_BYTES / ((r * TABLE_D + TABLE_V * r) * 2)))
+        sets = [(Q0, P0)] + [synthetic_head(torch, dev, TABLE_V, TABLE_D, r, 7000 + r + 97 * i, False)[:2]
+                             for i in range(1, R)]
+        for B in TABLE_B:
+            Hs = [synthetic_rows(torch, dev, B, TABLE_D, 9000 + 31 * i + B) for i in range(R)]
+            for k in TABLE_K:
+                ws = torch.empty(lr.load().lrhead_workspace_bytes(lr.BF16, TABLE_V, TABLE_D, r, B, k),
+                                 dtype=torch.uint8, device=dev)
+                heads = [lr.Head(Q, P, W, B_max=B, k_max=k, workspace=ws) for Q, P in sets]
+                out = (torch.empty((B, k), dtype=torch.int32, device=dev),
+                       torch.empty((B, k), dtype=torch.float32, device=dev),
+                       torch.empty((B, k), dtype=torch.float32, device=dev))
+                g = capture(torch, lambda i: heads[i % R].draft(Hs[i % R], k, out=out), R)
+                n = max(1, min(steps, int(4e5 // (B * 2 + 20))) // R)
+                g.replay()
+                us = timed_graph_replays(torch, g, n) / (n * R) * 1e6
+                rows.append({"B": B, "r": r, "k": k, "us_per_call": round(us, 2),
+                             "rows_per_s": round(B / (us * 1e-6), 1)})
+                if r == TABLE_R[0]:
+                    fo = (out[0], out[2])
+                    gf = capture(torch, lambda i: heads[0].full_topk(Hs[0], k, out=fo), 2)
+                    gf.replay()
+                    nf = max(1, min(60, int(2e4 // (B + 10))))
+                    usf = timed_graph_replays(torch, gf, nf) / (nf * 2) * 1e6
+                    full.append({"B": B, "k": k, "us_per_call": round(usf, 2)})
+                for h in heads:
+                    h.close()
+                del heads, ws, g
+        del sets, W
+        torch.cuda.empty_cache()
+    return {"table": "draft-head call latency, cache-cold graph replay", "V": TABLE_V, "d": TABLE_D,
+            "dtype": "bf16", "data": "synthetic (torch generator, workload recipe)",
+            "draft_head": rows, "full_head_baseline": full}
+
+
+def recall_sweep(torch, lr, dev, rows: int = 256) -> dict:
+    """Recall of the full head's top-b inside the low-rank top-k: for each r,
+    the share of each row's b best full-head tokens (exact logits over all V)
+    that the low-rank candidates of that row contain, averaged over rows."""
+    out = []
+    H = synthetic_rows(torch, dev, rows, TABLE_D, 4242)
+    for r in TABLE_R:
+        Q, P, W = synthetic_head(torch, dev, TABLE_V, TABLE_D, r, seed=7000 + r)
+        head = lr.Head(Q, P, W, B_max=rows, k_max=64)
+        cidx, _ = head.candidates(H, 64)
+        fidx, _ = head.full_topk(H, 8)
+        c = cidx.cpu().numpy()
+        f = fidx.cpu().numpy()
+        for b in (1, 4, 8):
+            for k in (8, 16, 32, 64):
+                hit = [len(set(f[i, :b].tolist()) & set(c[i, :k].tolist())) / b for i in range(rows)]
+                out.append({"r": r, "b": b, "k": k, "recall": round(float(sum(hit) / rows), 4)})
+        head.close()
+        del head, Q, P, W
+        torch.cuda.empty_cache()
+    return {"recall": "share of the full head's top-b found in the low-rank top-k", "V": TABLE_V,
+            "d": TABLE_D, "rows": rows, "noise": "W = P.Q + 0.1 E", "data": "synthetic", "results": out}
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -196,6 +301,14 @@ def main() -> int:
                                    "timed on a single MI355X, with no collectives; the multi-GPU sharding "
                                    "is a design note only. Run with --gpus 1."}), flush=True)
         return 2
+    if args.table or args.recall:
+        import torch
+        import rank_lm_head_amd as lr
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        res = latency_table(torch, lr, dev, args.steps) if args.table else recall_sweep(torch, lr, dev)
+        print(json.dumps(res), flush=True)
+        return 0
 
     import numpy as np
     import torch
