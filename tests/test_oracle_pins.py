@@ -454,3 +454,59 @@ def test_distribution_against_a_plain_loop():
         e = [math.exp(x - m) for x in l[b]]
         s = math.fsum(e)
         assert np.allclose(p[b], [x / s for x in e], rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------ building P and Q (F1-F4)
+
+def _spectrum_matrix(rng, V, d, sigma):
+    """U diag(sigma) V^T with random orthonormal U (V x n), V (d x n)."""
+    n = len(sigma)
+    U, _ = np.linalg.qr(rng.normal(size=(V, n)))
+    Vt, _ = np.linalg.qr(rng.normal(size=(d, n)))
+    return (U * np.asarray(sigma)) @ Vt.T
+
+
+def test_factor_recovers_an_exactly_low_rank_w():
+    """W of rank r exactly: P.Q = W (before the final rounding), P orthonormal."""
+    from oracle import factor as fa
+    rng = np.random.default_rng(11)
+    V, d, r = 600, 80, 12
+    W = rng.normal(size=(V, r)) @ rng.normal(size=(r, d))
+    omega = rng.normal(size=(d, r))
+    for q in (0, 1):
+        P, Q = fa.factor(W, omega, q, "fp64", round_out=False)
+        assert np.allclose(P @ Q, W, rtol=0, atol=1e-9 * np.abs(W).max())
+        assert np.allclose(P.T @ P, np.eye(r), atol=1e-12)
+
+
+def test_factor_error_approaches_the_truncated_svd_optimum():
+    """A known decaying spectrum: the error of P.Q is at least the Eckart-Young
+    optimum sqrt(sum of the discarded sigma^2) (numpy.linalg.svd agrees with
+    the construction) and comes within 2% of it after two iterations."""
+    from oracle import factor as fa
+    rng = np.random.default_rng(12)
+    V, d, r = 500, 120, 10
+    sigma = 1.0 / (1.0 + np.arange(60)) ** 1.2
+    W = _spectrum_matrix(rng, V, d, sigma)
+    s_np = np.linalg.svd(W, compute_uv=False)
+    assert np.allclose(s_np[:60], sigma, rtol=1e-10)
+    opt = math.sqrt(float(np.sum(sigma[r:] ** 2)))
+    omega = rng.normal(size=(d, r))
+    errs = []
+    for q in (0, 1, 2):
+        P, Q = fa.factor(W, omega, q, "fp64", round_out=False)
+        errs.append(np.linalg.norm(W - P @ Q))
+        assert errs[-1] >= opt * (1 - 1e-12)
+    assert errs[2] <= errs[0] and errs[2] <= 1.02 * opt, (errs, opt)
+
+
+def test_factor_orth_is_cholesky_qr2():
+    """orth() returns orthonormal columns spanning the input (its R factor is
+    triangular), checked against numpy's Householder QR."""
+    from oracle import factor as fa
+    rng = np.random.default_rng(13)
+    X = rng.normal(size=(300, 9)) * np.logspace(0, 3, 9)    # condition number ~1e3
+    Y = fa.orth(X)
+    assert np.allclose(Y.T @ Y, np.eye(9), atol=1e-13)
+    Qh, _ = np.linalg.qr(X)
+    assert np.allclose(np.abs(Y.T @ Qh), np.eye(9), atol=1e-10)    # same columns up to sign
