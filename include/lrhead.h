@@ -174,6 +174,28 @@ int lrhead_branch(const float* logits, const int32_t* idx, const float* parent,
                   float* br_prob, float* br_path, void* stream);
 
 /*
+ * Builds a low-rank head from a full-rank one (the pages factor token
+ * prediction into smaller matrices, "EAGLE-4 Triples Qwen3 Inference Speed
+ * by Adapting to Serving Load", section "Runtime-sized speculation", but do
+ * not say how): a randomized range finder with q subspace iterations,
+ *   Y = orth(W . omega);  q times: Z = orth(W^T . Y), Y = orth(W . Z);
+ *   P = Y (V x r, orthonormal columns),  Q = Y^T . W (r x d),
+ * orth() being CholeskyQR2 with fp64 Gram matrices, so P . Q is W projected
+ * onto the captured column space (exactly W when W has rank r).
+ * W: V x d bf16; omega: d x r fp32 (the Gaussian test matrix, supplied by the
+ * caller); P: V x r and Q: r x d bf16 outputs; all device pointers, 16-byte
+ * aligned, row-major. Requirements: 1 <= r <= min(512, d, V), 0 <= q <= 8,
+ * workspace of at least lrhead_factor_workspace_bytes(V, d, r) bytes.
+ * Asynchronous on `stream`; it may allocate nothing and synchronises nothing.
+ * A Gram matrix that is not positive definite (W of rank below r) gets tiny
+ * pivots, and P is then not orthonormal in the missing directions.
+ */
+size_t lrhead_factor_workspace_bytes(int64_t V, int64_t d, int r);
+int lrhead_factor(const void* W, int64_t V, int64_t d, int r, int q,
+                  const float* omega, void* P, void* Q, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
  * Profiling aid: hipEvent_t handles (passed as void*) that later calls on
  * this handle attach to the dispatch of the vocabulary score pass
  * (lrhead_candidates, lrhead_draft, fullhead_topk; for row batches its main

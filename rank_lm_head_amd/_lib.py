@@ -29,6 +29,9 @@ SIGNATURES = {
     "fullhead_topk": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp, _vp, _vp]),
     "lrhead_draft": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp, _vp, _vp, _vp]),
     "lrhead_branch": (ctypes.c_int, [_vp, _vp, _vp, _c_i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]),
+    "lrhead_factor_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, ctypes.c_int]),
+    "lrhead_factor": (ctypes.c_int, [_vp, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp]),
     "lrhead_set_stage_events": (ctypes.c_int, [_vp, _vp, _vp]),
     "lrhead_destroy": (None, [_vp]),
     "lrhead_strerror": (ctypes.c_char_p, [ctypes.c_int]),

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblrhead.so")
 SOURCES = ["kernels_small.hip", "kernels_mfma.hip", "kernels_gemm.hip", "kernels_merge.hip", "kernels_branch.hip",
-           "lrhead.hip"]
+           "kernels_factor.hip", "lrhead.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,0 +1,335 @@
+// kernels_factor.hip — building the low-rank head (P, Q) from W.
+//
+// The pages say token prediction is factored into smaller matrices ("EAGLE-4
+// Triples Qwen3 Inference Speed by Adapting to Serving Load", section
+// "Runtime-sized speculation") but not how the factors are made. This builds
+// them from W by a randomized range finder with subspace iteration (Halko,
+// Martinsson and Tropp's randomized low-rank approximation):
+//
+//   Y = orth(W . Omega);  q times: Z = orth(W^T . Y), Y = orth(W . Z);
+//   P = Y (V x r, orthonormal columns),  Q = Y^T . W (r x d)
+//
+// so that P . Q is the projection of W onto the captured column space.
+// orth() is CholeskyQR2: G = X^T X (accumulated in fp64), its Cholesky
+// factor G = L L^T, X <- X L^-T, twice.
+//
+// Kernels (vector ALU; the contractions are tall-skinny and need fp32 or
+// fp64 operands for the orthonormalisation):
+//   fgemm_kernel    C = op(A) . B for 64 x 64 tiles of C, K in chunks of 16
+//                   staged through LDS, 4 x 4 outputs per thread; A is W
+//                   (bf16) or an fp32 panel, read as is (M x K) or transposed
+//                   (stored K x M); long K runs as split-K partials
+//   reduce_kernel   sums the split-K partials
+//   chol_kernel     Cholesky of an n x n Gram matrix, one block, fp64
+//   trinv_kernel    the rows of L^-T (= columns of L^-1), one thread per
+//                   column, forward substitution, written as fp32
+//   cast kernels    P and Q in bf16 (Q transposed from W^T . Y)
+#include "launch.h"
+
+namespace lrh {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ld_f32(const T* p);
+template <>
+__device__ __forceinline__ float ld_f32<uint16_t>(const uint16_t* p) {
+  return __uint_as_float((uint32_t)*p << 16);
+}
+template <>
+__device__ __forceinline__ float ld_f32<float>(const float* p) {
+  return *p;
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {   // round to nearest even (finite inputs)
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+constexpr int kTile = 64;
+constexpr int kTk = 16;
+constexpr int kGemmThreads = 256;
+
+// Partial z of C (M x N, row-major) = op(A)[:, Kz] . B[Kz, :] with
+// Kz = [z * kchunk, min(K, (z + 1) * kchunk)). op(A) is M x K: A itself
+// (AT = false, A[m * lda + k]) or A transposed (AT = true, A[k * lda + m]).
+// B is K x N row-major (B[k * ldb + n]). Out-of-range elements load as 0.
+template <typename TA, bool AT, typename ACC>
+__global__ void __launch_bounds__(kGemmThreads) fgemm_kernel(const TA* __restrict__ A, int64_t lda,
+                                                             const float* __restrict__ Bm, int64_t ldb,
+                                                             ACC* __restrict__ C, int M, int N, int64_t K,
+                                                             int64_t kchunk) {
+  __shared__ ACC As[kTk][kTile + 1];
+  __shared__ ACC Bs[kTk][kTile + 1];
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int m0 = blockIdx.x * kTile, n0 = blockIdx.y * kTile;
+  const int64_t kb = (int64_t)blockIdx.z * kchunk;
+  const int64_t ke = kb + kchunk < K ? kb + kchunk : K;
+  ACC acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0;
+  for (int64_t k0 = kb; k0 < ke; k0 += kTk) {
+#pragma unroll
+    for (int q = 0; q < kTile * kTk / kGemmThreads; ++q) {
+      const int e = q * kGemmThreads + threadIdx.x;
+      int kk, mm;
+      if (AT) {
+        kk = e / kTile;
+        mm = e % kTile;
+      } else {
+        mm = e / kTk;
+        kk = e % kTk;
+      }
+      const int64_t gk = k0 + kk;
+      const int gm = m0 + mm;
+      float v = 0.f;
+      if (gk < ke && gm < M) v = ld_f32<TA>(AT ? A + gk * lda + gm : A + (int64_t)gm * lda + gk);
+      As[kk][mm] = (ACC)v;
+      const int kb2 = e / kTile, nn = e % kTile;
+      const int64_t gk2 = k0 + kb2;
+      const int gn = n0 + nn;
+      Bs[kb2][nn] = (ACC)((gk2 < ke && gn < N) ? Bm[gk2 * ldb + gn] : 0.f);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kTk; ++kk) {
+      ACC a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
+  }
+  ACC* Cz = C + (int64_t)blockIdx.z * M * N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n < N) Cz[(int64_t)m * N + n] = acc[i][j];
+    }
+  }
+}
+
+// out[i] = sum over z < S of part[z * count + i]
+template <typename ACC>
+__global__ void __launch_bounds__(256) reduce_kernel(const ACC* __restrict__ part, int S, int64_t count,
+                                                     ACC* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+    ACC s = 0;
+    for (int z = 0; z < S; ++z) s += part[(int64_t)z * count + i];
+    out[i] = s;
+  }
+}
+
+// In place: the lower triangle of G (n x n, row-major, symmetric) becomes L
+// with G = L L^T (right-looking, one column per step). A pivot that is not
+// positive (a rank-deficient panel) is replaced by a tiny one and counted in
+// *status.
+constexpr int kCholThreads = 1024;
+__global__ void __launch_bounds__(kCholThreads) chol_kernel(double* __restrict__ G, int n,
+                                                           uint32_t* __restrict__ status) {
+  __shared__ double piv;
+  for (int j = 0; j < n; ++j) {
+    if (threadIdx.x == 0) {
+      double d = G[(int64_t)j * n + j];
+      if (!(d > 0.0)) {
+        atomicAdd(status, 1u);
+        d = 1e-300;
+      }
+      piv = sqrt(d);
+      G[(int64_t)j * n + j] = piv;
+    }
+    __syncthreads();
+    const double s = piv;
+    for (int i = j + 1 + threadIdx.x; i < n; i += kCholThreads) G[(int64_t)i * n + j] /= s;
+    __syncthreads();
+    // trailing update of the lower triangle: rows i > j, columns j < c <= i
+    const int m = n - j - 1;
+    for (int64_t t = threadIdx.x; t < (int64_t)m * m; t += kCholThreads) {
+      const int i = j + 1 + (int)(t / m), c = j + 1 + (int)(t % m);
+      if (c <= i) G[(int64_t)i * n + c] -= G[(int64_t)i * n + j] * G[(int64_t)c * n + j];
+    }
+    __syncthreads();
+  }
+}
+
+// Rd = L^-T (fp64) and Rinv = L^-T (fp32), n x n row-major: thread c solves
+// L x = e_c by forward substitution; x is column c of L^-1, i.e. row c of
+// L^-T, kept in fp64 in Rd while it is built.
+__global__ void __launch_bounds__(256) trinv_kernel(const double* __restrict__ L, int n, double* __restrict__ Rd,
+                                                    float* __restrict__ Rinv) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= n) return;
+  double* x = Rd + (int64_t)c * n;
+  float* row = Rinv + (int64_t)c * n;
+  for (int i = 0; i < c; ++i) {
+    x[i] = 0.0;
+    row[i] = 0.f;
+  }
+  x[c] = 1.0 / L[(int64_t)c * n + c];
+  row[c] = (float)x[c];
+  for (int i = c + 1; i < n; ++i) {
+    double s = 0.0;
+    for (int j = c; j < i; ++j) s += L[(int64_t)i * n + j] * x[j];
+    x[i] = -s / L[(int64_t)i * n + i];
+    row[i] = (float)x[i];
+  }
+}
+
+__global__ void zero_kernel(uint32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
+
+// P = bf16(Y) (V x r); Q[i][j] = bf16(Z[j][i]) (Z: d x r, Q: r x d)
+__global__ void __launch_bounds__(256) cast_p_kernel(const float* __restrict__ Y, int64_t n, uint16_t* __restrict__ P) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    P[i] = to_bf16(Y[i]);
+}
+__global__ void __launch_bounds__(256) cast_q_kernel(const float* __restrict__ Z, int d, int r,
+                                                     uint16_t* __restrict__ Q) {
+  const int64_t n = (int64_t)d * r;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n; t += (int64_t)gridDim.x * 256) {
+    const int i = (int)(t / d), j = (int)(t % d);   // Q[i][j], coalesced writes
+    Q[t] = to_bf16(Z[(int64_t)j * r + i]);
+  }
+}
+
+struct FactorWs {
+  float* Y[2];      // V x r
+  float* Z[2];      // d x r
+  float* part;      // split-K partials (fp32), kSplitMax x max(V, d) x r ... sized below
+  double* partd;    // split-K partials of Gram matrices (fp64)
+  double* G;        // r x r
+  double* Rd;       // r x r
+  float* Rinv;      // r x r
+  uint32_t* status;
+};
+
+constexpr int kSplitZ = 16;     // splits of K = V for W^T . Y
+
+// Splits of a Gram matrix X^T X (r x r, K = rows): about 2048 blocks in all.
+int gram_splits(int r) {
+  const int tiles = ((r + kTile - 1) / kTile) * ((r + kTile - 1) / kTile);
+  int s = 2048 / tiles;
+  return s < 8 ? 8 : (s > 256 ? 256 : s);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t ws_layout(int64_t V, int64_t d, int r, FactorWs* w, char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  FactorWs t;
+  t.Y[0] = (float*)take((size_t)V * r * 4);
+  t.Y[1] = (float*)take((size_t)V * r * 4);
+  t.Z[0] = (float*)take((size_t)d * r * 4);
+  t.Z[1] = (float*)take((size_t)d * r * 4);
+  t.part = (float*)take((size_t)kSplitZ * d * r * 4);
+  t.partd = (double*)take((size_t)gram_splits(r) * r * r * 8);
+  t.G = (double*)take((size_t)r * r * 8);
+  t.Rd = (double*)take((size_t)r * r * 8);
+  t.Rinv = (float*)take((size_t)r * r * 4);
+  t.status = (uint32_t*)take(256);
+  if (w) *w = t;
+  return off;
+}
+
+template <typename TA, bool AT, typename ACC>
+hipError_t gemm(const TA* A, int64_t lda, const float* B, int64_t ldb, ACC* C, int M, int N, int64_t K, int S,
+                hipStream_t s) {
+  const int64_t kchunk = ((K + S - 1) / S + kTk - 1) / kTk * kTk;
+  const int Sz = (int)((K + kchunk - 1) / kchunk);
+  dim3 grid((unsigned)((M + kTile - 1) / kTile), (unsigned)((N + kTile - 1) / kTile), (unsigned)Sz);
+  hipLaunchKernelGGL((fgemm_kernel<TA, AT, ACC>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, C, M, N, K, kchunk);
+  return hipGetLastError();
+}
+
+int splits_for(int64_t K, int S) {
+  const int64_t kchunk = ((K + S - 1) / S + kTk - 1) / kTk * kTk;
+  return (int)((K + kchunk - 1) / kchunk);
+}
+
+#define LRH_F(x)                          \
+  do {                                    \
+    const hipError_t e_ = (x);            \
+    if (e_ != hipSuccess) return e_;      \
+  } while (0)
+
+// X (rows x r, fp32) <- orth(X) by CholeskyQR2; X and T are the two buffers
+// of the panel, the result ends in X.
+hipError_t orth(float*& X, float*& T, int64_t rows, int r, const FactorWs& w, hipStream_t s) {
+  for (int pass = 0; pass < 2; ++pass) {
+    int S = (int)((rows + 255) / 256);
+    if (S > gram_splits(r)) S = gram_splits(r);
+    const int Sz = splits_for(rows, S);
+    LRH_F((gemm<float, true, double>(X, r, X, r, w.partd, r, r, rows, S, s)));
+    hipLaunchKernelGGL(reduce_kernel<double>, dim3((unsigned)(((int64_t)r * r + 255) / 256)), dim3(256), 0, s,
+                       w.partd, Sz, (int64_t)r * r, w.G);
+    LRH_F(hipGetLastError());
+    hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(kCholThreads), 0, s, w.G, r, w.status);
+    LRH_F(hipGetLastError());
+    hipLaunchKernelGGL(trinv_kernel, dim3((unsigned)((r + 255) / 256)), dim3(256), 0, s, w.G, r, w.Rd, w.Rinv);
+    LRH_F(hipGetLastError());
+    // T = X . L^-T: (rows x r) . (r x r)
+    LRH_F((gemm<float, false, float>(X, r, w.Rinv, r, T, (int)rows, r, r, 1, s)));
+    float* t = X;
+    X = T;
+    T = t;
+  }
+  return hipSuccess;
+}
+
+// Z = W^T . Y (d x r), reduced into Zout
+hipError_t wt_times(const uint16_t* W, int64_t V, int64_t d, int r, const float* Y, float* Zout, const FactorWs& w,
+                    hipStream_t s) {
+  const int Sz = splits_for(V, kSplitZ);
+  LRH_F((gemm<uint16_t, true, float>(W, d, Y, r, w.part, (int)d, r, V, kSplitZ, s)));
+  hipLaunchKernelGGL(reduce_kernel<float>, dim3((unsigned)((d * r + 255) / 256)), dim3(256), 0, s, w.part, Sz,
+                     (int64_t)d * r, Zout);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t factor_workspace_bytes(int64_t V, int64_t d, int r) { return ws_layout(V, d, r, nullptr, nullptr); }
+
+hipError_t launch_factor(const void* Wv, int64_t V, int64_t d, int r, int q, const float* omega, void* Pv, void* Qv,
+                         void* workspace, hipStream_t s) {
+  const uint16_t* W = static_cast<const uint16_t*>(Wv);
+  FactorWs w;
+  ws_layout(V, d, r, &w, static_cast<char*>(workspace));
+  hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, w.status, 1);
+  LRH_F(hipGetLastError());
+  float *Y = w.Y[0], *Yt = w.Y[1], *Z = w.Z[0], *Zt = w.Z[1];
+  // Y = orth(W . Omega)
+  LRH_F((gemm<uint16_t, false, float>(W, d, omega, r, Y, (int)V, r, d, 1, s)));
+  LRH_F(orth(Y, Yt, V, r, w, s));
+  for (int it = 0; it < q; ++it) {
+    LRH_F(wt_times(W, V, d, r, Y, Z, w, s));
+    LRH_F(orth(Z, Zt, d, r, w, s));
+    LRH_F((gemm<uint16_t, false, float>(W, d, Z, r, Y, (int)V, r, d, 1, s)));
+    LRH_F(orth(Y, Yt, V, r, w, s));
+  }
+  // P = Y, Q = (W^T . Y)^T
+  LRH_F(wt_times(W, V, d, r, Y, Z, w, s));
+  hipLaunchKernelGGL(cast_p_kernel, dim3(2048), dim3(256), 0, s, Y, V * r, static_cast<uint16_t*>(Pv));
+  LRH_F(hipGetLastError());
+  hipLaunchKernelGGL(cast_q_kernel, dim3(2048), dim3(256), 0, s, Z, (int)d, r, static_cast<uint16_t*>(Qv));
+  return hipGetLastError();
+}
+
+}  // namespace lrh

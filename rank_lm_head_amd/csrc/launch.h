@@ -117,6 +117,13 @@ hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n
 hipError_t launch_branch(const float* logits, const int32_t* idx, const float* parent, int64_t B, int k, int nb,
                          float* probs, int32_t* br_idx, float* br_prob, float* br_path, hipStream_t stream);
 
+// ---------------------------------------------------- kernels_factor.hip
+// P (V x r) and Q (r x d), bf16, from W (V x d, bf16) by a randomized range
+// finder with q subspace iterations; omega is d x r fp32.
+size_t factor_workspace_bytes(int64_t V, int64_t d, int r);
+hipError_t launch_factor(const void* W, int64_t V, int64_t d, int r, int q, const float* omega, void* P, void* Q,
+                         void* workspace, hipStream_t stream);
+
 // logits[b, j] = W[idx[b, j], :] . h_b (NaN for ids outside [0, V)).
 hipError_t launch_rescore(int dtype, const void* W, const void* H, const int32_t* idx, int64_t B,
                           int k, int64_t V, int d, float* logits, hipStream_t stream);

@@ -323,6 +323,29 @@ int lrhead_branch(const float* logits, const int32_t* idx, const float* parent, 
   return LRHEAD_OK;
 }
 
+size_t lrhead_factor_workspace_bytes(int64_t V, int64_t d, int r) {
+  if (V < 1 || d < 1 || r < 1 || r > LRHEAD_R_MAX || r > d || r > V || V > INT32_MAX || d > LRHEAD_D_MAX) return 0;
+  return lrh::factor_workspace_bytes(V, d, r);
+}
+
+int lrhead_factor(const void* W, int64_t V, int64_t d, int r, int q, const float* omega, void* P, void* Q,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (V < 1 || V > INT32_MAX) return fail(LRHEAD_ERANGE, "V = %lld outside [1, 2^31)", (long long)V);
+  if (d < 1 || d > LRHEAD_D_MAX) return fail(LRHEAD_ERANGE, "d = %lld outside [1, %d]", (long long)d, LRHEAD_D_MAX);
+  if (r < 1 || r > LRHEAD_R_MAX || r > d || r > V)
+    return fail(LRHEAD_ERANGE, "r = %d outside [1, min(%d, d, V)]", r, LRHEAD_R_MAX);
+  if (q < 0 || q > 8) return fail(LRHEAD_ERANGE, "q = %d outside [0, 8]", q);
+  if (!W || !omega || !P || !Q || !workspace)
+    return fail(LRHEAD_EINVAL, "W, omega, P, Q and workspace must be non-NULL");
+  if (!aligned16(W) || !aligned16(omega) || !aligned16(P) || !aligned16(Q) || !aligned16(workspace))
+    return fail(LRHEAD_EALIGN, "W, omega, P, Q and workspace must be 16-byte aligned");
+  const size_t need = lrh::factor_workspace_bytes(V, d, r);
+  if (workspace_bytes < need) return fail(LRHEAD_EWORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, need);
+  LRH_HIP(lrh::launch_factor(W, V, d, r, q, omega, P, Q, workspace, static_cast<hipStream_t>(stream)),
+          "factor launch");
+  return LRHEAD_OK;
+}
+
 int lrhead_set_stage_events(lrhead_t h, void* before, void* after) {
   LRH_TRY(check_handle(h));
   if ((before == nullptr) != (after == nullptr))

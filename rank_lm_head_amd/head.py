@@ -175,3 +175,24 @@ def branch(logits: torch.Tensor, idx: torch.Tensor, nb: int, parent: torch.Tenso
     _lib.check(lib.lrhead_branch(_ptr(logits), _ptr(idx), _ptr(parent), B, k, nb, _ptr(probs), _ptr(br_idx),
                                  _ptr(br_prob), _ptr(br_path), stream), "lrhead_branch")
     return probs, br_idx, br_prob, br_path
+
+
+def factor(W: torch.Tensor, r: int, omega: torch.Tensor, q: int = 1):
+    """A low-rank head (P: [V, r], Q: [r, d], bf16) built from W ([V, d], bf16)
+    with the Gaussian test matrix omega ([d, r], float32); q subspace
+    iterations. See lrhead_factor in include/lrhead.h."""
+    _need(W.is_cuda and W.dtype == torch.bfloat16 and W.dim() == 2 and W.is_contiguous(),
+          "W must be a contiguous bfloat16 device matrix")
+    V, d = W.shape
+    _need(omega.is_cuda and omega.dtype == torch.float32 and tuple(omega.shape) == (d, r) and omega.is_contiguous(),
+          f"omega must be a contiguous float32 device tensor of shape ({d}, {r})")
+    lib = _lib.load()
+    nbytes = lib.lrhead_factor_workspace_bytes(V, d, r)
+    _need(nbytes > 0, f"r = {r} outside [1, min(512, d, V)]")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    P = torch.empty((V, r), dtype=torch.bfloat16, device=W.device)
+    Q = torch.empty((r, d), dtype=torch.bfloat16, device=W.device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(W.device).cuda_stream)
+    _lib.check(lib.lrhead_factor(_ptr(W), V, d, r, q, _ptr(omega), _ptr(P), _ptr(Q), _ptr(ws), nbytes, stream),
+               "lrhead_factor")
+    return P, Q

@@ -113,3 +113,17 @@ def test_python_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         lr.Head(Q, torch.zeros(100, 16, dtype=torch.bfloat16), torch.zeros(100, 64, dtype=torch.bfloat16),
                 B_max=1, k_max=4)
+
+
+def test_factor_validates_on_the_host():
+    lib = _lib.load()
+    assert lib.lrhead_factor_workspace_bytes(151936, 5120, 128) > 0
+    assert lib.lrhead_factor_workspace_bytes(100, 64, 65) == 0        # r > d
+    assert lib.lrhead_factor_workspace_bytes(100, 64, 0) == 0
+    p = ctypes.c_void_p(0x20000)
+    n = lib.lrhead_factor_workspace_bytes(1000, 64, 8)
+    assert lib.lrhead_factor(p, 1000, 64, 513, 1, p, p, p, p, n, None) == _lib.ERANGE
+    assert lib.lrhead_factor(p, 1000, 64, 8, 9, p, p, p, p, n, None) == _lib.ERANGE
+    assert lib.lrhead_factor(p, 1000, 64, 8, 1, None, p, p, p, n, None) == _lib.EINVAL
+    assert lib.lrhead_factor(p, 1000, 64, 8, 1, ctypes.c_void_p(0x20004), p, p, p, n, None) == _lib.EALIGN
+    assert lib.lrhead_factor(p, 1000, 64, 8, 1, p, p, p, p, n - 1, None) == _lib.EWORKSPACE

@@ -5,6 +5,7 @@ oracle's k-th/(k+1)-th gap exceeds 1e-3 * max|score|, boundary swaps only
 inside that band; logits within 2e-3 (bf16) or 1e-5 (fp32) relative.
 """
 import functools
+import math
 import sys
 
 import numpy as np
@@ -389,3 +390,69 @@ def test_branch_edge_cases():
         assert not errs, (nb, errs[:5])
     one = lr.branch(torch.tensor([[3.0]], device=DEV), torch.tensor([[17]], dtype=torch.int32, device=DEV), 1)
     assert np_(one[0]).tolist() == [[1.0]] and np_(one[1]).tolist() == [[17]]
+
+
+# ------------------------------------------------ building P and Q (F1-F4)
+
+def _bf16_np(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_factor_close(P_g, Q_g, P_o, Q_o):
+    """Device P, Q (bf16) against the oracle's (float64 values of bf16):
+    equal up to two bf16 steps of each value plus 1e-4 of the largest (the
+    device sums in fp32 where the oracle sums in float64; the final rounding
+    to bf16 can then land one step apart)."""
+    errs = []
+    for name, g, o in (("P", P_g, P_o), ("Q", Q_g, Q_o)):
+        tol = 2 * oracle.ulp_bf16(np.abs(o)) + 1e-4 * np.abs(o).max()
+        bad = np.abs(g - o) > tol
+        if bad.any():
+            errs.append(f"{name}: {int(bad.sum())} of {bad.size} elements off, worst {np.abs(g - o).max():.3g}")
+    return errs
+
+
+@pytest.mark.parametrize("V,d,r,q", [
+    (3000, 256, 32, 1),     # ragged tiles in V
+    (20000, 1024, 64, 2),   # two iterations
+    (4096, 200, 8, 0),      # no iteration, d not a multiple of 64
+])
+def test_factor_matches_the_oracle(V, d, r, q):
+    from oracle import factor as fa
+    rng = np.random.default_rng(V + r)
+    Wf = (rng.normal(size=(V, r)) @ rng.normal(size=(r, d)) / math.sqrt(d)
+          + 0.1 * rng.normal(size=(V, d)) / math.sqrt(d))
+    W = oracle.round_bf16(oracle.round_fp32(Wf))
+    Wb = (W.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    omega = rng.normal(size=(d, r)).astype(np.float32)
+    say(f"[run] factor V={V} d={d} r={r} q={q}")
+    P, Q = lr.factor(dev(Wb, DEV), r, torch.from_numpy(omega).to(DEV), q)
+    torch.cuda.synchronize()
+    P_o, Q_o = fa.factor(Wb, omega, q, "bf16")
+    P_g = oracle.to_f64(_bf16_np(P), "bf16")
+    Q_g = oracle.to_f64(_bf16_np(Q), "bf16")
+    errs = check_factor_close(P_g, Q_g, P_o, Q_o)
+    assert not errs, errs
+    e_g = np.linalg.norm(W - P_g @ Q_g)
+    e_o = np.linalg.norm(W - P_o @ Q_o)
+    assert abs(e_g - e_o) <= 1e-2 * e_o, (e_g, e_o)
+
+
+def test_factor_at_the_drafter_head_size():
+    """V = 151936, d = 5120, r = 128, q = 1 on the batch-1 workload's W: the
+    columns of P are orthonormal (to bf16 precision) and P.Q approximates W
+    at least as well as the generator's own rank-128 part P0.Q0 does."""
+    inp, t = config(2)
+    W = t["W"]
+    d, r = W.shape[1], 128
+    omega = torch.randn(d, r, generator=torch.Generator(DEV).manual_seed(1), device=DEV)
+    say("[run] factor at V=151936 d=5120 r=128")
+    P, Q = lr.factor(W, r, omega, 1)
+    torch.cuda.synchronize()
+    Pf, Qf, Wf = P.float(), Q.float(), W.float()
+    gram = Pf.T @ Pf
+    assert torch.allclose(gram, torch.eye(r, device=DEV), atol=2e-2), float((gram - torch.eye(r, device=DEV)).abs().max())
+    rows = torch.arange(0, W.shape[0], 97, device=DEV)
+    err = torch.linalg.norm(Wf[rows] - Pf[rows] @ Qf)
+    planted = torch.linalg.norm(Wf[rows] - t["P"][rows].float() @ t["Q"].float())
+    assert err <= 1.02 * planted, (float(err), float(planted))
