@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--table", action="store_true",
                     help="instead of the headline: a latency table of the draft-head call over "
                          "B x r x k (and of the full-head baseline over B x k), one JSON object")
+    ap.add_argument("--factor", action="store_true",
+                    help="instead of the headline: time building P and Q from W (r = 128/256/512, one "
+                         "subspace iteration) at V=151936, d=5120, one JSON object")
     ap.add_argument("--recall", action="store_true",
                     help="instead of the headline: recall of the full head's top-b inside the "
                          "low-rank top-k for r in 128/256/512, one JSON object")
@@ -293,6 +296,35 @@ def recall_sweep(torch, lr, dev, rows: int = 256) -> dict:
             "d": TABLE_D, "rows": rows, "noise": "W = P.Q + 0.1 E", "data": "synthetic", "results": out}
 
 
+def factor_timing(torch, lr, dev, reps: int = 3) -> dict:
+    """Wall time of lrhead_factor (one subspace iteration) per r, with the
+    work of its four W-sized products (W.Omega, W^T.Y, W.Z, W^T.Y: 2*V*d*r
+    flops each) as the rate, against the fp32 vector peak (the products run
+    on the vector ALU), and the relative error of P.Q on every 97th row."""
+    out = []
+    for r in TABLE_R:
+        _, _, W = synthetic_head(torch, dev, TABLE_V, TABLE_D, r, seed=7000 + r)
+        omega = torch.randn(TABLE_D, r, generator=torch.Generator(device=dev).manual_seed(r), device=dev)
+        P, Q = lr.factor(W, r, omega, 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            P, Q = lr.factor(W, r, omega, 1)
+        torch.cuda.synchronize()
+        s_per = (time.perf_counter() - t0) / reps
+        big = 4 * 2.0 * TABLE_V * TABLE_D * r
+        rows = torch.arange(0, TABLE_V, 97, device=dev)
+        Wf = W[rows].float()
+        rel = float(torch.linalg.norm(Wf - P[rows].float() @ Q.float()) / torch.linalg.norm(Wf))
+        out.append({"r": r, "q": 1, "ms": round(s_per * 1e3, 2),
+                    "w_products_tflops": round(big / s_per / 1e12, 2),
+                    "alu_frac": round(big / s_per / (157.3e12), 4), "rel_error": round(rel, 5)})
+        del W, P, Q
+        torch.cuda.empty_cache()
+    return {"factor": "P, Q from W by a randomized range finder, one subspace iteration", "V": TABLE_V,
+            "d": TABLE_D, "peak": "fp32 vector 157.3 TFLOP/s", "data": "synthetic", "results": out}
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -301,12 +333,17 @@ def main() -> int:
                                    "timed on a single MI355X, with no collectives; the multi-GPU sharding "
                                    "is a design note only. Run with --gpus 1."}), flush=True)
         return 2
-    if args.table or args.recall:
+    if args.table or args.recall or args.factor:
         import torch
         import rank_lm_head_amd as lr
         dev = torch.device("cuda:0")
         torch.cuda.set_device(dev)
-        res = latency_table(torch, lr, dev, args.steps) if args.table else recall_sweep(torch, lr, dev)
+        if args.table:
+            res = latency_table(torch, lr, dev, args.steps)
+        elif args.recall:
+            res = recall_sweep(torch, lr, dev)
+        else:
+            res = factor_timing(torch, lr, dev)
         print(json.dumps(res), flush=True)
         return 0
 

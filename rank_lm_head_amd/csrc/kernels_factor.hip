@@ -21,7 +21,7 @@
 //                   (stored K x M); long K runs as split-K partials
 //   reduce_kernel   sums the split-K partials
 //   chol_kernel     Cholesky of an n x n Gram matrix, one block, fp64
-//   trinv_kernel    the rows of L^-T (= columns of L^-1), one thread per
+//   trinv_kernel    the rows of L^-T (= columns of L^-1), one wave per
 //                   column, forward substitution, written as fp32
 //   cast kernels    P and Q in bf16 (Q transposed from W^T . Y)
 #include "launch.h"
@@ -132,57 +132,82 @@ __global__ void __launch_bounds__(256) reduce_kernel(const ACC* __restrict__ par
 }
 
 // In place: the lower triangle of G (n x n, row-major, symmetric) becomes L
-// with G = L L^T (right-looking, one column per step). A pivot that is not
-// positive (a rank-deficient panel) is replaced by a tiny one and counted in
-// *status.
+// with G = L L^T (right-looking, one column per step, two barriers a step:
+// every thread takes the pivot itself, scales its rows of the column and
+// copies them to LDS; after a barrier the trailing lower triangle is
+// updated from the LDS copy). A pivot that is not positive (a rank-deficient
+// panel) is replaced by a tiny one and counted in *status.
 constexpr int kCholThreads = 1024;
+constexpr int kCholMax = 512;
 __global__ void __launch_bounds__(kCholThreads) chol_kernel(double* __restrict__ G, int n,
                                                            uint32_t* __restrict__ status) {
-  __shared__ double piv;
+  __shared__ double col[kCholMax];
   for (int j = 0; j < n; ++j) {
-    if (threadIdx.x == 0) {
-      double d = G[(int64_t)j * n + j];
-      if (!(d > 0.0)) {
-        atomicAdd(status, 1u);
-        d = 1e-300;
-      }
-      piv = sqrt(d);
-      G[(int64_t)j * n + j] = piv;
+    double d = G[(int64_t)j * n + j];
+    if (!(d > 0.0)) {
+      if (threadIdx.x == 0) atomicAdd(status, 1u);
+      d = 1e-300;
+    }
+    const double piv = sqrt(d);
+    for (int i = j + 1 + threadIdx.x; i < n; i += kCholThreads) {
+      const double v = G[(int64_t)i * n + j] / piv;
+      G[(int64_t)i * n + j] = v;
+      col[i] = v;
     }
     __syncthreads();
-    const double s = piv;
-    for (int i = j + 1 + threadIdx.x; i < n; i += kCholThreads) G[(int64_t)i * n + j] /= s;
-    __syncthreads();
+    if (threadIdx.x == 0) G[(int64_t)j * n + j] = piv;   // every thread has read the old diagonal
     // trailing update of the lower triangle: rows i > j, columns j < c <= i
+    // (32-bit indices: n <= 512)
     const int m = n - j - 1;
-    for (int64_t t = threadIdx.x; t < (int64_t)m * m; t += kCholThreads) {
-      const int i = j + 1 + (int)(t / m), c = j + 1 + (int)(t % m);
-      if (c <= i) G[(int64_t)i * n + c] -= G[(int64_t)i * n + j] * G[(int64_t)c * n + j];
+    for (int t = threadIdx.x; t < m * m; t += kCholThreads) {
+      const int i = j + 1 + t / m, c = j + 1 + t % m;
+      if (c <= i) G[i * n + c] -= col[i] * col[c];
     }
     __syncthreads();
   }
 }
 
-// Rd = L^-T (fp64) and Rinv = L^-T (fp32), n x n row-major: thread c solves
-// L x = e_c by forward substitution; x is column c of L^-1, i.e. row c of
-// L^-T, kept in fp64 in Rd while it is built.
-__global__ void __launch_bounds__(256) trinv_kernel(const double* __restrict__ L, int n, double* __restrict__ Rd,
-                                                    float* __restrict__ Rinv) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= n) return;
-  double* x = Rd + (int64_t)c * n;
+// Rinv = L^-T (fp32), n x n row-major. Wave c solves L x = e_c by forward
+// substitution (x is column c of L^-1, i.e. row c of L^-T): x_c = 1 / L_cc,
+// then for each i > c the dot product of row i of L with x so far, taken by
+// the whole wave (lanes stride over j) and reduced by DPP and two shuffles;
+// x is kept in fp64 in LDS.
+constexpr int kInvWaves = 4;
+constexpr int kInvMax = 512;
+__global__ void __launch_bounds__(kInvWaves * 64) trinv_kernel(const double* __restrict__ L, int n,
+                                                               float* __restrict__ Rinv) {
+  __shared__ double xs[kInvWaves][kInvMax];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * kInvWaves + wave;
+  if (c >= n) return;   // whole waves
+  double* x = xs[wave];
   float* row = Rinv + (int64_t)c * n;
-  for (int i = 0; i < c; ++i) {
-    x[i] = 0.0;
-    row[i] = 0.f;
-  }
-  x[c] = 1.0 / L[(int64_t)c * n + c];
-  row[c] = (float)x[c];
+  for (int i = lane; i < c; i += 64) row[i] = 0.f;
+  const double xc = 1.0 / L[(int64_t)c * n + c];
+  if (lane == 0) x[c] = xc;
+  if (lane == 0) row[c] = (float)xc;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   for (int i = c + 1; i < n; ++i) {
+    const double* Li = L + (int64_t)i * n;
     double s = 0.0;
-    for (int j = c; j < i; ++j) s += L[(int64_t)i * n + j] * x[j];
-    x[i] = -s / L[(int64_t)i * n + i];
-    row[i] = (float)x[i];
+    for (int j = c + lane; j < i; j += 64) s += Li[j] * x[j];
+    // wave sum in fp64 by butterfly shuffles
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 8);
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    const double xi = -s / Li[i];
+    if (lane == 0) {
+      x[i] = xi;
+      row[i] = (float)xi;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -210,7 +235,6 @@ struct FactorWs {
   float* part;      // split-K partials (fp32), kSplitMax x max(V, d) x r ... sized below
   double* partd;    // split-K partials of Gram matrices (fp64)
   double* G;        // r x r
-  double* Rd;       // r x r
   float* Rinv;      // r x r
   uint32_t* status;
 };
@@ -241,7 +265,6 @@ size_t ws_layout(int64_t V, int64_t d, int r, FactorWs* w, char* base) {
   t.part = (float*)take((size_t)kSplitZ * d * r * 4);
   t.partd = (double*)take((size_t)gram_splits(r) * r * r * 8);
   t.G = (double*)take((size_t)r * r * 8);
-  t.Rd = (double*)take((size_t)r * r * 8);
   t.Rinv = (float*)take((size_t)r * r * 4);
   t.status = (uint32_t*)take(256);
   if (w) *w = t;
@@ -282,7 +305,8 @@ hipError_t orth(float*& X, float*& T, int64_t rows, int r, const FactorWs& w, hi
     LRH_F(hipGetLastError());
     hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(kCholThreads), 0, s, w.G, r, w.status);
     LRH_F(hipGetLastError());
-    hipLaunchKernelGGL(trinv_kernel, dim3((unsigned)((r + 255) / 256)), dim3(256), 0, s, w.G, r, w.Rd, w.Rinv);
+    hipLaunchKernelGGL(trinv_kernel, dim3((unsigned)((r + kInvWaves - 1) / kInvWaves)), dim3(kInvWaves * 64), 0, s,
+                       w.G, r, w.Rinv);
     LRH_F(hipGetLastError());
     // T = X . L^-T: (rows x r) . (r x r)
     LRH_F((gemm<float, false, float>(X, r, w.Rinv, r, T, (int)rows, r, r, 1, s)));
@@ -310,6 +334,7 @@ size_t factor_workspace_bytes(int64_t V, int64_t d, int r) { return ws_layout(V,
 hipError_t launch_factor(const void* Wv, int64_t V, int64_t d, int r, int q, const float* omega, void* Pv, void* Qv,
                          void* workspace, hipStream_t s) {
   const uint16_t* W = static_cast<const uint16_t*>(Wv);
+  if (r > kCholMax || r > kInvMax) return hipErrorInvalidValue;
   FactorWs w;
   ws_layout(V, d, r, &w, static_cast<char*>(workspace));
   hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, w.status, 1);
