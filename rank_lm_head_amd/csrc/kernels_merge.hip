@@ -39,13 +39,15 @@ __device__ __forceinline__ float dot_chunk<float>(u32x4 w, u32x4 h, float acc) {
   return acc;
 }
 
-// w . h over d elements by one wave; every lane returns the sum. Up to 16
-// wave loads of each operand are in flight; loads past d read a clamped,
-// valid address and are zeroed, so none is predicated.
-template <typename T>
-__device__ __forceinline__ float wave_row_dot(const T* __restrict__ w, const T* __restrict__ h, int d) {
+// w . h over d elements by one wave; every lane returns the sum. A row of
+// up to U wave loads has all of them in flight (U is the row's load count
+// rounded up to 4, 8, 10, 12 or 16, so that no load is wasted on a short
+// row); longer rows go in chunks of 16. Loads past d read a clamped, valid
+// address and are zeroed, so none is predicated. For every U the lane's
+// sum runs over its chunks in the same order.
+template <typename T, int U>
+__device__ __forceinline__ float wave_row_dot_u(const T* __restrict__ w, const T* __restrict__ h, int d) {
   constexpr int per = 16 / sizeof(T);
-  constexpr int U = 16;
   const int lane = threadIdx.x & 63;
   float acc = 0.f;
   for (int c0 = 0; c0 < d; c0 += U * kWave * per) {
@@ -64,6 +66,17 @@ __device__ __forceinline__ float wave_row_dot(const T* __restrict__ w, const T* 
     }
   }
   return group_sum<kWave>(acc);
+}
+
+template <typename T>
+__device__ __forceinline__ float wave_row_dot(const T* __restrict__ w, const T* __restrict__ h, int d) {
+  constexpr int per = 16 / sizeof(T);
+  const int nl = (d + kWave * per - 1) / (kWave * per);   // wave loads per row
+  if (nl <= 4) return wave_row_dot_u<T, 4>(w, h, d);
+  if (nl <= 8) return wave_row_dot_u<T, 8>(w, h, d);
+  if (nl <= 10) return wave_row_dot_u<T, 10>(w, h, d);
+  if (nl <= 12) return wave_row_dot_u<T, 12>(w, h, d);
+  return wave_row_dot_u<T, 16>(w, h, d);
 }
 
 // ------------------------------------------------------------ rescoring

@@ -138,49 +138,53 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
   const int64_t whi = blo + (bhi - blo) * (wave + 1) / kWavesSmall;
 
   // The wave's rows go in groups of STEP (U wave loads), two groups in
-  // flight: group g + 1 is issued before group g is used. The groups are
-  // unrolled with fixed buffers (no register copies, which would wait for
-  // the loads in flight), and the last group prefetches nothing, so no load
-  // is outstanding after the pass. Rows past the wave's range are loaded
+  // flight: group g + 1 is issued before group g is used. The loop takes two
+  // groups per iteration with fixed buffers (no register copies, which would
+  // wait for the loads in flight); the last group prefetches nothing, so no
+  // load is outstanding after the pass. Rows past the wave's range are loaded
   // from its last row (a valid address, so no load is predicated) and never
   // kept (a wave without rows loads row 0).
-  constexpr int NGM = (E * kWave / kWavesSmall + STEP - 1) / STEP;   // most groups of a wave
   const int64_t last = whi > 0 ? whi - 1 : 0;
   const int ng = wlo < whi ? (int)((whi - wlo + STEP - 1) / STEP) : 0;
-  u32x4 buf[2][U];
-  auto issue = [&](int q, int64_t base) {
+  u32x4 buf0[U], buf1[U];
+  auto issue = [&](u32x4 (&buf)[U], int64_t base) {
 #pragma unroll
     for (int t = 0; t < U; ++t) {
       const int64_t row = base + t * RPL + sub;
-      buf[q][t] = load16(M + (row < last ? row : last) * K + 8 * c);
+      buf[t] = load16(M + (row < last ? row : last) * K + 8 * c);
     }
   };
-  auto consume = [&](int q, int64_t base) {
+  auto consume = [&](const u32x4 (&buf)[U], int64_t base) {
 #pragma unroll
     for (int t = 0; t < U; ++t) {
       const int64_t row = base + t * RPL + sub;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         if (b >= B) break;
-        const float s = group_sum<LPR>(dot8_bf16(buf[q][t], zc[b], 0.f));
+        const float s = group_sum<LPR>(dot8_bf16(buf[t], zc[b], 0.f));
         if (c == 0 && row < whi) sc[b][row - blo] = s;
       }
     }
   };
-  issue(0, wlo);   // unconditional: a branch here would make the first use wait for every load
+  issue(buf0, wlo);   // unconditional: a branch here would make the first use wait for every load
   __builtin_amdgcn_sched_barrier(0);   // all of them before anything waits for z
 #pragma unroll
   for (int b = 0; b < NB; ++b) zc[b] = widen8(b < B ? zr[b] : u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-  for (int g = 0; g < NGM; ++g) {
+  int g = 0;
+  for (; g + 2 < ng; g += 2) {   // buf0 holds group g on entry
     const int64_t base = wlo + (int64_t)g * STEP;
-    if (g + 1 < ng) {
-      issue((g + 1) & 1, base + STEP);
-      consume(g & 1, base);
-    } else {
-      if (g < ng) consume(g & 1, base);
-      break;
-    }
+    issue(buf1, base + STEP);
+    consume(buf0, base);
+    issue(buf0, base + 2 * STEP);
+    consume(buf1, base + STEP);
+  }
+  if (g + 1 < ng) {
+    const int64_t base = wlo + (int64_t)g * STEP;
+    issue(buf1, base + STEP);
+    consume(buf0, base);
+    consume(buf1, base + STEP);
+  } else if (g < ng) {
+    consume(buf0, wlo + (int64_t)g * STEP);
   }
   __syncthreads();
   const int nrows = (int)(bhi - blo);
