@@ -360,13 +360,15 @@ __global__ void __launch_bounds__(256) theta_kernel(const float* __restrict__ tm
 }
 
 // ----------------------------------------------------------------- collect
-// One wave per row (four rows per block). The row's mask words are read in
-// chunks of 16-byte loads; each lane counts its flags, and a prefix over
-// the lanes (from the bit planes of the counts) gives every flag a slot.
-// Flagged vocabulary ids go to LDS, then their scores are fetched in
-// batches (independent loads) and ranked. A row with more than kColCap
-// flags (ties) is taken in rounds of kColCap slots, each round's best k
-// merged into a running list.
+// One block per row. The four waves split the row's mask words (16-byte
+// loads, a round's words in flight together); the flagged ids go to an LDS
+// buffer (a slot from a prefix over the wave's lanes, the wave's base from
+// an LDS counter: the order is free, the keys are ranked), then the wave
+// fetches their scores in batches and stores their keys. Wave 0 then ranks
+// the buffer.
+// A row with more than kColCap flags (ties) is taken by wave 0 alone in
+// rounds of kColCap slots (collect_rounds), each round's best k merged into
+// a running list.
 constexpr int kColCap = 1024;
 constexpr int kColE = kColCap / kWave;
 
@@ -379,15 +381,10 @@ struct CollectWave {
 };
 
 template <int TM>
-__global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* __restrict__ mask, int NW,
-                                                                const float* __restrict__ S, int64_t ldS, int64_t B,
-                                                                int k, int32_t* __restrict__ idx,
-                                                                float* __restrict__ score) {
-  __shared__ CollectWave cw[4];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= B) return;
-  CollectWave& m = cw[wave];
+__device__ __forceinline__ void collect_rounds(CollectWave& m, const uint32_t* __restrict__ mask, int NW,
+                                               const float* __restrict__ S, int64_t ldS, int64_t row, int k,
+                                               int32_t* __restrict__ idx, float* __restrict__ score) {
+  const int lane = threadIdx.x & 63;
   const uint32_t* mw = mask + row * NW;
   const float* sr = S + row * ldS;
 
@@ -489,6 +486,112 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
   }
 }
 
+
+template <int TM>
+__global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* __restrict__ mask, int NW,
+                                                                const float* __restrict__ S, int64_t ldS, int64_t B,
+                                                                int k, int32_t* __restrict__ idx,
+                                                                float* __restrict__ score) {
+  __shared__ CollectWave m;
+  __shared__ int n_flag;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = blockIdx.x;
+  const uint32_t* mw = mask + row * NW;
+  const float* sr = S + row * ldS;
+  if (threadIdx.x == 0) n_flag = 0;
+  __syncthreads();
+  // wave w takes the 16-byte word groups q = w * per + [0, per), in rounds of
+  // T4 per lane
+  constexpr int T4 = 4;
+  const int nq = (NW + 3) / 4;
+  const int per = (nq + 3) / 4;
+  const int q0 = wave * per, q1 = min(nq, q0 + per);
+  for (int qb = q0; qb < q1; qb += kWave * T4) {
+    u32x4 wd[T4];
+#pragma unroll
+    for (int t = 0; t < T4; ++t) {
+      const int q = qb + t * kWave + lane;
+      wd[t] = *reinterpret_cast<const u32x4*>(mw + 4 * min(q, nq - 1));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (q >= q1 || 4 * q + e >= NW) wd[t][e] = 0u;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int t = 0; t < T4; ++t) cnt += __popc(wd[t][0]) + __popc(wd[t][1]) + __popc(wd[t][2]) + __popc(wd[t][3]);
+    int before = 0, total = 0;
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {   // at most 4 * T4 * 32 = 512 flags per lane
+      const unsigned long long plane = __ballot((cnt >> bit) & 1);
+      before += lanes_below(plane) << bit;
+      total += __popcll(plane) << bit;
+    }
+    const unsigned long long hi = __ballot(cnt >> 8);
+    if (hi) total += kColCap + 1;   // cannot happen with distinct scores; forces the rounds
+    int base = 0;
+    if (lane == 0 && total) base = atomicAdd(&n_flag, total);
+    base = __builtin_amdgcn_readfirstlane(base);
+    int pos = base + before;
+#pragma unroll
+    for (int t = 0; t < T4; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t bits = wd[t][e];
+        const int w = 4 * (qb + t * kWave + lane) + e;
+        const int64_t slice = w >> 2, gq = w & 3;
+        while (bits) {
+          const int b = __builtin_ctz(bits);
+          bits &= bits - 1;
+          if (pos < kColCap) m.vid[pos] = (int)(slice * TM + (b >> 2) * 16 + 4 * gq + (b & 3));
+          ++pos;
+        }
+      }
+    }
+    // the scores of this round's slots [base, base + total), loads in batches
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int send = min(base + total, kColCap);
+    for (int s0 = base; s0 < send; s0 += 8 * kWave) {
+      int vv[8];
+      float xs[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sl = s0 + u * kWave + lane;
+        vv[u] = sl < send ? m.vid[sl] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) xs[u] = sr[vv[u]];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sl = s0 + u * kWave + lane;
+        if (sl < send) m.key[sl] = cand_key(xs[u], vv[u]);
+      }
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int C = n_flag;
+  if (C > kColCap) {
+    collect_rounds<TM>(m, mask, NW, S, ldS, row, k, idx, score);
+    return;
+  }
+  uint64_t key[kColE];
+#pragma unroll
+  for (int e = 0; e < kColE; ++e) {
+    const int j = e * kWave + lane;
+    key[e] = j < C ? m.key[j] : 0ull;
+  }
+  wave_topk_emit<kColE>(key, k, m.tmp, m.ls[1], m.li[1]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < k) {
+    idx[row * k + lane] = m.li[1][lane];
+    if (score) score[row * k + lane] = m.ls[1][lane];
+  }
+}
+
 // ================================================================ launchers
 
 namespace {
@@ -572,7 +675,7 @@ hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, in
   e = run_gemm<C>(kModeFilter, M, X, V, K, B, (int)p.nvb, 1, nullptr, 0, w.theta, w.S, p.ldS, w.mask, p.NW,
                   stream, t);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(collect_kernel<C::TM>, dim3((unsigned)((B + 3) / 4)), dim3(kGemmThreads), 0, stream, w.mask,
+  hipLaunchKernelGGL(collect_kernel<C::TM>, dim3((unsigned)B), dim3(kGemmThreads), 0, stream, w.mask,
                      p.NW, w.S, p.ldS, B, k, idx, score);
   return hipGetLastError();
 }
