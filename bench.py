@@ -204,7 +204,7 @@ def cpu_baseline(inp: dict, seconds: float) -> dict:
 # RMS-normalised. (The headline and the parity tests use the numpy
 # generator of gen/; the sweeps need many shapes quickly.)
 TABLE_V, TABLE_D = 151936, 5120
-TABLE_B = (1, 8, 64, 256, 2048)
+TABLE_B = (1, 4, 8, 16, 64, 256, 2048)
 TABLE_R = (128, 256, 512)
 TABLE_K = (8, 32, 64)
 
@@ -447,8 +447,8 @@ def main() -> int:
     # bound by whichever of HBM and MFMA its arithmetic intensity points to.
     sel_bytes = cfg.V * cfg.r * s + cfg.B * cfg.r * s
     sel_flops = 2.0 * cfg.B * cfg.V * cfg.r
-    batch = cfg.dtype == "bf16" and cfg.B > 4
-    small = cfg.dtype == "bf16" and cfg.B <= 4 and cfg.r in (8, 16, 32, 64, 128, 256, 512)
+    small = cfg.dtype == "bf16" and cfg.B <= 8 and cfg.r in (8, 16, 32, 64, 128, 256, 512)
+    batch = cfg.dtype == "bf16" and cfg.B > 4 and not small
     if batch:
         sel_kernel, what = "gemm_sel_kernel", "main GEMM pass: scores of all rows, flagged above the sampled bound"
     elif small:

@@ -682,7 +682,7 @@ hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, in
 
 }  // namespace
 
-bool batch_path(int dtype, int64_t B) { return dtype == 0 && B > kSmallB; }
+bool batch_path(int dtype, int64_t B) { return dtype == 0 && B > kLongB; }
 
 hipError_t batch_init() {
   hipError_t e = allow_lds<CfgWide>();

@@ -1,6 +1,7 @@
-// kernels_small.hip — the head for a few draft rows (B <= 4), bf16.
+// kernels_small.hip — the head for a few rows, bf16: draft calls with B <= 8,
+// the full-head baseline with B <= 4.
 //
-// With one to four rows both contractions are matrix-vector products and
+// With one to eight rows both contractions are matrix-vector products and
 // the time is HBM streaming ("EAGLE-4", section "Retrieve vocabulary
 // candidates cheaply, then score them exactly": the low-rank head still
 // scores every vocabulary row, so P is read once per call). Matrix cores
@@ -28,33 +29,44 @@ constexpr int kSmallThreads = kWavesSmall * kWave;
 // A row of Q is NL wave loads of 1 KiB (d <= NL * 512); all of them and the
 // matching chunks of h are issued before the products. Loads past d read a
 // clamped, valid address and are zeroed afterwards, so no load is predicated.
+// The rows of h go in chunks of up to four (their loads for eight rows would
+// not fit in registers next to the row of Q); later chunks hit in L2.
 template <int NB, int NL>
 __global__ void __launch_bounds__(kSmallThreads) down_small_kernel(const uint16_t* __restrict__ Q,
                                                                    const uint16_t* __restrict__ H, int r,
                                                                    int d, int B, uint16_t* __restrict__ Z) {
+  constexpr int CH = NB < 4 ? NB : 4;
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int j = blockIdx.x * kWavesSmall + wave;
   if (j >= r) return;
   const uint16_t* q = Q + (int64_t)j * d;
-  u32x4 qv[NL], hv[NB][NL];
+  u32x4 qv[NL];
+  int cols[NL];
 #pragma unroll
   for (int t = 0; t < NL; ++t) {
     const int c = (t * kWave + lane) * 8;
-    const int cc = c < d ? c : d - 8;
-    qv[t] = load16(q + cc);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) hv[b][t] = load16(H + (int64_t)(b < B ? b : 0) * d + cc);
+    cols[t] = c < d ? c : d - 8;
+    qv[t] = load16(q + cols[t]);
   }
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    float acc = 0.f;
+  for (int b0 = 0; b0 < NB; b0 += CH) {
+    if (b0 >= B) break;
+    u32x4 hv[CH][NL];
 #pragma unroll
-    for (int t = 0; t < NL; ++t) {
-      const bool ok = (t * kWave + lane) * 8 < d;
-      acc = dot8_bf16(ok ? qv[t] : u32x4{0u, 0u, 0u, 0u}, hv[b][t], acc);
+    for (int t = 0; t < NL; ++t)
+#pragma unroll
+      for (int b = 0; b < CH; ++b) hv[b][t] = load16(H + (int64_t)(b0 + b < B ? b0 + b : 0) * d + cols[t]);
+#pragma unroll
+    for (int b = 0; b < CH; ++b) {
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < NL; ++t) {
+        const bool ok = (t * kWave + lane) * 8 < d;
+        acc = dot8_bf16(ok ? qv[t] : u32x4{0u, 0u, 0u, 0u}, hv[b][t], acc);
+      }
+      const float z = group_sum<kWave>(acc);
+      if (b0 + b < B && lane == 0) Z[(int64_t)(b0 + b) * r + j] = f32_to_bf16(z);
     }
-    const float z = group_sum<kWave>(acc);
-    if (b < B && lane == 0) Z[(int64_t)b * r + j] = f32_to_bf16(z);
   }
 }
 
@@ -188,21 +200,23 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
   }
   __syncthreads();
   const int nrows = (int)(bhi - blo);
-  if (wave < B) {
-    const int64_t o = (int64_t)wave * L * nblk + blockIdx.x;
-    wave_top_few<E>(sc[wave], nrows, (int)blo, L, part_s + o, part_i + o, nblk);
-  }
-  // The raw scores: the waves without a row copy all rows; when every wave
-  // has a row (B = 4), each copies its own after its selection.
-  const int idle = kWavesSmall - B;
-  const int t0 = idle > 0 ? (wave - B) * kWave + lane : lane;
-  const int step = idle > 0 ? idle * kWave : kWave;
-  if (idle == 0 || wave >= B) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b >= B) break;
-      if (idle == 0 && b != wave) continue;
-      for (int j = t0; j < nrows; j += step) raw[(int64_t)b * V + blo + j] = sc[b][j];
+  if (B < kWavesSmall) {
+    // wave b selects for row b; the waves without a row copy every row's
+    // raw scores
+    if (wave < B) {
+      const int64_t o = (int64_t)wave * L * nblk + blockIdx.x;
+      wave_top_few<E>(sc[wave], nrows, (int)blo, L, part_s + o, part_i + o, nblk);
+    } else {
+      const int t0 = (wave - B) * kWave + lane, step = (kWavesSmall - B) * kWave;
+      for (int b = 0; b < B; ++b)
+        for (int j = t0; j < nrows; j += step) raw[(int64_t)b * V + blo + j] = sc[b][j];
+    }
+  } else {
+    // wave w takes rows w, w + 4: the selection, then the raw copy
+    for (int b = wave; b < B; b += kWavesSmall) {
+      const int64_t o = (int64_t)b * L * nblk + blockIdx.x;
+      wave_top_few<E>(sc[b], nrows, (int)blo, L, part_s + o, part_i + o, nblk);
+      for (int j = lane; j < nrows; j += kWave) raw[(int64_t)b * V + blo + j] = sc[b][j];
     }
   }
 }
@@ -285,7 +299,7 @@ bool small_path(int dtype, int64_t B, int64_t K_lowrank, int64_t V) {
 constexpr int kMaxRowLoads = 16;   // rows up to 8192 elements
 
 bool small_long_path(int dtype, int64_t B, int64_t K, int64_t V) {
-  return dtype == 0 && B <= kSmallB && K <= kMaxRowLoads * kWave * 8 &&
+  return dtype == 0 && B <= kLongB && K <= kMaxRowLoads * kWave * 8 &&
          V <= (int64_t)kMaxSmallBlocks * kBlockRows;
 }
 
@@ -313,21 +327,34 @@ static int row_loads(int K) {
     }                                   \
   } while (0)
 
-#define LRH_NB_DISPATCH(B, body) \
+// Rows per launch, rounded up to an instantiated count: 1, 2, 4 (and 8 for
+// the kernels that take eight rows).
+#define LRH_NB4_DISPATCH(B, ...) \
   do {                           \
     if ((B) <= 1) {              \
       constexpr int NB = 1;      \
-      body;                      \
+      __VA_ARGS__;               \
     } else if ((B) == 2) {       \
       constexpr int NB = 2;      \
-      body;                      \
+      __VA_ARGS__;               \
     } else {                     \
       constexpr int NB = 4;      \
-      body;                      \
+      __VA_ARGS__;               \
     }                            \
   } while (0)
 
+#define LRH_NB_DISPATCH(B, ...)          \
+  do {                                   \
+    if ((B) <= kLongB) {                 \
+      LRH_NB4_DISPATCH(B, __VA_ARGS__);  \
+    } else {                             \
+      constexpr int NB = 8;              \
+      __VA_ARGS__;                       \
+    }                                    \
+  } while (0)
+
 hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream) {
+  if (B < 1 || B > kSmallB) return hipErrorInvalidValue;
   dim3 grid((r + kWavesSmall - 1) / kWavesSmall);
   const int nl = row_loads(d);
   if (nl < 0) return launch_down(0, Q, H, r, d, B, Z, stream);   // rows longer than 8192
@@ -346,7 +373,7 @@ static hipError_t launch_short_k(const void* M, const void* X, int64_t V, int64_
   dim3 grid(nblk);
   const int64_t rows = (V + nblk - 1) / nblk;   // most rows of one block
   const int L = small_list_len(k);
-  if (rows > 8 * kWave || V * nblk >= (int64_t)1 << 32) return hipErrorInvalidValue;
+  if (B < 1 || B > kSmallB || rows > 8 * kWave || V * nblk >= (int64_t)1 << 32) return hipErrorInvalidValue;
   if (rows <= 4 * kWave) {
     LRH_NB_DISPATCH(B, LRH_LAUNCH(t, (select_short_kernel<K, NB, 4>), grid, dim3(kSmallThreads), 0, stream,
                                   (const uint16_t*)M, (const uint16_t*)X, V, (int)B, L, ps, pi, raw));
@@ -376,10 +403,10 @@ hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, i
 
 hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* ps,
                               int* pi, hipStream_t stream, Timing t) {
-  if (V > (int64_t)kMaxSmallBlocks * kBlockRows) return hipErrorInvalidValue;
+  if (B > kLongB || V > (int64_t)kMaxSmallBlocks * kBlockRows) return hipErrorInvalidValue;
   dim3 grid(small_blocks(V));
   const int nl = row_loads(K);
-  LRH_NB_DISPATCH(B, LRH_NL_DISPATCH(nl, LRH_LAUNCH(t, (select_long_kernel<NB, NL>), grid, dim3(kSmallThreads), 0,
+  LRH_NB4_DISPATCH(B, LRH_NL_DISPATCH(nl, LRH_LAUNCH(t, (select_long_kernel<NB, NL>), grid, dim3(kSmallThreads), 0,
                                                     stream, (const uint16_t*)M, (const uint16_t*)X, V, K, (int)B, k,
                                                     ps, pi)));
   return hipGetLastError();

@@ -24,9 +24,11 @@ struct Timing {
       hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);                         \
   } while (0)
 
-// Draft-row counts up to this use the streaming (vector ALU) kernels of
-// kernels_small.hip; larger batches use the matrix-core kernels.
-constexpr int kSmallB = 4;
+// Draft calls with up to kSmallB rows, and full-head calls with up to kLongB
+// rows, use the streaming (vector ALU) kernels of kernels_small.hip; larger
+// bf16 batches use the matrix-core kernels.
+constexpr int kSmallB = 8;
+constexpr int kLongB = 4;
 
 // ----------------------------------------------------- kernels_small.hip
 // Blocks (= candidate lists per row) of the streaming selection over V rows.
@@ -35,7 +37,7 @@ int small_blocks(int64_t V);
 bool small_path(int dtype, int64_t B, int64_t K, int64_t V);
 bool small_long_path(int dtype, int64_t B, int64_t K, int64_t V);
 
-// z = round(Q . h) for B <= 4 rows.
+// z = round(Q . h) for B <= kSmallB rows.
 hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream);
 // Streaming score pass: per block, the small_list_len(k) best of its slice
 // for each row, written depth-major (entry j of block x's list at
@@ -66,8 +68,9 @@ hipError_t launch_dense(int dtype, const void* W, const void* H, int64_t V, int 
                         float* logits, hipStream_t stream);
 
 // ------------------------------------------------------ kernels_gemm.hip
-// bf16 row batches (B > kSmallB) take the matrix-core GEMM with a sampled
-// per-row bound and an exact collect (no per-slice lists).
+// bf16 row batches (B > kLongB) that the streaming path does not take use
+// the matrix-core GEMM with a sampled per-row bound and an exact collect (no
+// per-slice lists).
 bool batch_path(int dtype, int64_t B);
 
 struct BatchPlan {

@@ -28,7 +28,7 @@ struct lrhead_s {
   void* z;          // B_max x r, weight dtype
   float* part_s;    // candidate lists: rows x slices x k_max
   int* part_i;
-  float* raw;       // raw scores of the streaming path: min(B_max, 4) x V
+  float* raw;       // raw scores of the streaming path: min(B_max, 8) x V
   bool batch;       // bf16 with B_max > 4: the GEMM path's scratch exists
   lrh::BatchScratch bw;
   hipEvent_t ev_before;  // optional events attached to the score pass: its start
@@ -148,7 +148,8 @@ lrh::Timing timing(const lrhead_s* h) { return lrh::Timing{h->ev_before, h->ev_a
 // the slice lists; with `logits`, the merge also rescores the winners.
 int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, float* score, float* logits,
                  hipStream_t s) {
-  if (lrh::batch_path(h->dtype, B)) {
+  const bool streaming = lrh::small_path(h->dtype, B, h->r, h->V);
+  if (!streaming && lrh::batch_path(h->dtype, B)) {
     // many rows: the down-projection is a GEMM worth the pipelined kernel
     if (B >= kDownGemmRows)
       LRH_HIP(lrh::launch_down_gemm(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
@@ -162,7 +163,7 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   }
   int n_lists, list_len = k;
   const float* raw = nullptr;
-  if (lrh::small_path(h->dtype, B, h->r, h->V)) {
+  if (streaming) {
     LRH_HIP(lrh::launch_down_small(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
     LRH_HIP(lrh::launch_select_small(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, h->raw, s,
                                      timing(h)),

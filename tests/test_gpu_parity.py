@@ -102,6 +102,13 @@ def test_small_heads(dt, V, d, r, B, k):
     (777, 64, 32, 1, 5),
     (300, 1032, 8, 2, 3),        # k < 4, r = 8, d not a multiple of 512
     (9000, 8200, 64, 1, 16),     # d beyond the long-row kernel: matrix-core full head
+    (5000, 256, 128, 5, 64),     # five rows: the eight-row kernels with three idle rows
+    (30000, 512, 256, 8, 40),    # eight rows, many blocks
+    (777, 64, 32, 6, 5),
+    (300, 1032, 8, 7, 3),        # seven rows, r = 8, d not a multiple of 512
+    (9000, 8200, 64, 8, 16),     # eight rows with d beyond the streaming down-projection
+    (30000, 5120, 512, 8, 64),   # eight rows at the drafter head's d, r at its maximum
+    (200000, 64, 32, 8, 16),     # 391 rows per slice: the deepest score buffer
 ])
 def test_streaming_path_shapes(V, d, r, B, k):
     inp = gen.make_custom(V, d, r, B, "bf16", seed=V + r)
@@ -286,7 +293,7 @@ def test_duplicate_rows_tie_to_the_lower_id():
     assert len(set(np_(flog)[0].tolist())) == 1
 
 
-@pytest.mark.parametrize("B", [1, 4])
+@pytest.mark.parametrize("B", [1, 4, 8])
 def test_ties_inside_one_slice_go_to_the_lower_ids(B):
     """Bitwise copies of the best low-rank row inside one vocabulary slice, at
     ids that share a lane and ids in different lanes: every tied copy must come
