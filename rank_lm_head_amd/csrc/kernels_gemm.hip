@@ -592,6 +592,223 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
   }
 }
 
+// ------------------------------------------------ short-K vocabulary pass
+// For the low-rank scores K = r <= 256, so a lane's share of a 64-row
+// operand tile over the whole K fits in registers (KT * 4 16-byte
+// fragments). A block then keeps its BN draft rows of X (= z) in LDS for its
+// whole life and streams strips of 256 vocabulary rows of M past them:
+//  - wave w owns rows [64 w, 64 w + 64) of a strip (four 16-row tiles), and
+//    reads their K columns straight from global memory into the A operands
+//    of the matrix cores;
+//  - the A operands of four k steps are held in registers: once a k step's
+//    MFMAs are issued, its registers are refilled with the k step four
+//    ahead (in this strip or the block's next one), so the loads run about
+//    half a strip ahead of their use (no LDS stage for M);
+//  - the B operands (X) come from LDS, chunk c of row n at c ^ (n & 15).
+// Blocks are persistent: block (grp, nt) takes strips grp, grp + G, ... for
+// batch tile nt. When several batch tiles exist, the NT blocks of one strip
+// group sit on one XCD (consecutive workgroup ids go to consecutive XCDs),
+// so a strip comes from HBM once and from that XCD's L2 after.
+// K past the row (K % 32 != 0) meets zero X chunks, so every product there
+// is an exact zero. M rows past V read as zeros and are never flagged.
+// Both passes of a selection (sample and main) run on this kernel, so each
+// 16x16 tile of scores comes out of the same MFMA sequence in both, and the
+// bound of the sample pass holds bit for bit in the main pass.
+// Strip s covers vocabulary rows [s * stride * 256, s * stride * 256 + 256).
+//  kModeMax:    tile maxima, row n at aux_f + n * ns_tiles, index s * 16 +
+//               w * 4 + i for the 16-row tile i of wave w;
+//  kModeFilter: per-row bound theta; flagged scores into S (row n at
+//               S + n * ldS) and one mask word per (row, 64-row slice,
+//               lane group): word (vb * 4 + w) * 4 + g holds bit i * 4 + q
+//               for vocabulary row (vb * 4 + w) * 64 + i * 16 + 4 * g + q.
+constexpr int kStripRows = 256;
+
+template <int BN, int KT, int MODE>
+__global__ void __launch_bounds__(kGemmThreads) strip_sel_kernel(
+    const uint16_t* __restrict__ M, const uint16_t* __restrict__ X, int64_t V, int K, int64_t B, int nstrips,
+    int stride, int G, float* __restrict__ aux_f, int ns_tiles, const float* __restrict__ theta,
+    float* __restrict__ S, int64_t ldS, uint32_t* __restrict__ mask, int NW) {
+  constexpr int NF = BN / 16;                   // 16-column tiles of draft rows
+  constexpr int CH = KT * 4;                    // 16-byte chunks per X row in LDS
+  constexpr int SW = (CH < 16 ? CH : 16) - 1;   // swizzle mask
+  extern __shared__ u32x4 xs[];                 // [BN][CH]
+
+  const int NT = (int)((B + BN - 1) / BN);
+  const int Lb = blockIdx.x;
+  int grp, nt;
+  if (NT > 1 && G % kXcds == 0) {
+    const int xcd = Lb % kXcds, j = Lb / kXcds;
+    grp = (j / NT) * kXcds + xcd;
+    nt = j % NT;
+  } else {
+    grp = Lb / NT;
+    nt = Lb % NT;
+  }
+  const int64_t n0 = (int64_t)nt * BN;
+
+  // X tile to LDS, eight loads in flight per thread (clamped addresses,
+  // zeros selected after the loads, so none of them waits on another)
+  {
+    constexpr int NL = BN * CH / kGemmThreads, NB = NL < 8 ? NL : 8;
+    static_assert(NL * kGemmThreads == BN * CH && NL % NB == 0, "whole chunks per thread");
+#pragma unroll
+    for (int e0 = 0; e0 < NL; e0 += NB) {
+      u32x4 v[NB];
+      bool ok[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int e = (e0 + u) * kGemmThreads + threadIdx.x;
+        const int n = e / CH, c = e % CH;
+        ok[u] = n0 + n < B && c * 8 < K;
+        v[u] = load16(X + (ok[u] ? (n0 + n) * K + c * 8 : 0));
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int e = (e0 + u) * kGemmThreads + threadIdx.x;
+        const int n = e / CH, c = e % CH;
+        xs[n * CH + (c ^ (n & SW))] = ok[u] ? v[u] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  // the bound of each of the block's draft rows (main pass), read per
+  // column tile in the epilogue
+  __shared__ float th_s[MODE == kModeFilter ? BN : 1];
+  if constexpr (MODE == kModeFilter) {
+    for (int n = threadIdx.x; n < BN; n += kGemmThreads) th_s[n] = theta[n0 + n < B ? n0 + n : B - 1];
+  }
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+  __syncthreads();
+  if (grp >= nstrips) return;
+
+  // M rows of a strip through a buffer resource whose base and size are
+  // the strip's (scalar registers): the lane's offsets do not change
+  // between strips, and rows past V lie outside the resource and read as
+  // zeros. Columns past K read the next row's first columns (finite) or
+  // zeros; they meet zero X chunks either way.
+  const uint32_t lane_off = (uint32_t)(((wave * 64 + col) * K + g * 8) * 2);
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = lane_off + (uint32_t)(i * 16 * K * 2);
+  auto strip_rsrc = [&](int s) {
+    const int64_t row0 = (int64_t)s * stride * kStripRows;
+    const int64_t rows = V - row0 < kStripRows ? V - row0 : kStripRows;
+    const uint64_t addr = reinterpret_cast<uint64_t>(M + row0 * K);
+    const uint64_t ua = ((uint64_t)uniform_u32((uint32_t)(addr >> 32)) << 32) | uniform_u32((uint32_t)addr);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ua), (short)0,
+                                             (int)uniform_u32((uint32_t)(rows * K * 2)), kRawBufferFlags);
+  };
+
+  // A operands of the next KW k steps in a ring: slot t % KW holds k step
+  // t; once its MFMAs are issued it is refilled with k step t + KW, of this
+  // strip or of the block's next one.
+  constexpr int KW = KT < 4 ? KT : 4;
+  u32x4 a[KW][4];
+  {
+    const __amdgpu_buffer_rsrc_t rs = strip_rsrc(grp);
+#pragma unroll
+    for (int t = 0; t < KW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[t][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[i] + t * 64, 0, 0);
+  }
+
+  for (int s = grp; s < nstrips; s += G) {
+    const int sn = s + G < nstrips ? s + G : s;   // the last strip reloads itself (in bounds, unused)
+    const __amdgpu_buffer_rsrc_t rc = strip_rsrc(s), rn = strip_rsrc(sn);
+
+    f32x4 acc[4][NF];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jn = 0; jn < NF; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The X fragments do not change between strips. When they fit in 64
+    // registers the compiler keeps them there for the block's life; above
+    // that they are read from LDS two fragments ahead of their MFMAs (the
+    // empty asm keeps the reads from being hoisted out of the strip loop).
+    if constexpr (KT * NF > 16) asm volatile("" ::: "memory");
+    constexpr int NU = KT * NF;
+    auto xfrag = [&](int u) {
+      const int t = u / NF, jn = u % NF;
+      return xs[(jn * 16 + col) * CH + ((t * 4 + g) ^ (col & SW))];
+    };
+    u32x4 b0 = xfrag(0), b1 = NU > 1 ? xfrag(1) : b0;
+    __builtin_amdgcn_sched_group_barrier(0x100, NU > 1 ? 2 : 1, 0);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int t = u / NF, jn = u % NF;
+      u32x4 b2 = b1;
+      if (u + 2 < NU) {
+        b2 = xfrag(u + 2);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // the read two fragments ahead
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i][jn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[t % KW][i]),
+                                                             __builtin_bit_cast(bf16x8, b0), acc[i][jn], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (jn == NF - 1) {
+        // k step t is done with its slot: k step t + KW takes its place
+        const int tn = t + KW;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          a[t % KW][i] = tn < KT ? __builtin_amdgcn_raw_buffer_load_b128(rc, voff[i] + tn * 64, 0, 0)
+                                 : __builtin_amdgcn_raw_buffer_load_b128(rn, voff[i] + (tn - KT) * 64, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+      }
+      b0 = b1;
+      b1 = b2;
+    }
+
+    // ------------------------------------------------------------ epilogue
+    const int64_t vb = (int64_t)s * stride;
+    const int64_t vrow = vb * kStripRows + wave * 64 + 4 * g;   // + i * 16 + q
+    if constexpr (MODE == kModeMax) {
+#pragma unroll
+      for (int jn = 0; jn < NF; ++jn) {
+        const int64_t n = n0 + jn * 16 + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float m = neg_inf();
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (vrow + i * 16 + q < V) m = fmaxf(m, acc[i][jn][q]);
+          m = fmax_lanes(m);
+          if (g == 0 && n < B) aux_f[n * ns_tiles + s * 16 + wave * 4 + i] = m;
+        }
+      }
+    } else {
+      uint32_t valid = 0xFFFFu;
+      if (vb * kStripRows + kStripRows > V) {
+        valid = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) valid |= (vrow + i * 16 + q < V ? 1u : 0u) << (i * 4 + q);
+      }
+#pragma unroll
+      for (int jn = 0; jn < NF; ++jn) {
+        const int64_t n = n0 + jn * 16 + col;
+        const float th = th_s[jn * 16 + col];
+        uint32_t bits = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bits |= (acc[i][jn][q] >= th ? 1u : 0u) << (i * 4 + q);
+        bits &= valid;
+        if (n >= B) continue;
+        mask[n * NW + (vb * 4 + wave) * 4 + g] = bits;
+        if (bits == 0) continue;
+        float* srow = S + n * ldS + vrow;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((bits >> (i * 4)) & 15u) *reinterpret_cast<f32x4*>(srow + i * 16) = acc[i][jn];
+      }
+    }
+  }
+}
+
 // ================================================================ launchers
 
 namespace {
@@ -652,14 +869,10 @@ hipError_t run_gemm(int mode, const uint16_t* M, const uint16_t* X, int64_t V, i
   return hipGetLastError();
 }
 
-template <class C>
-hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, int64_t V, int K, int64_t B, int k,
-                    const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream, Timing t) {
-  hipError_t e = run_gemm<C>(kModeMax, M, X, V, K, B, p.ns, p.stride, w.tmax, p.ns_tiles, nullptr, nullptr, 0,
-                             nullptr, 0, stream);
-  if (e != hipSuccess) return e;
-  // the bound need not be the exact k-th maximum: any value that between k
-  // and cap maxima reach is valid (a looser one flags more scores)
+// theta of every row from the sample pass's tile maxima. The bound need not
+// be the exact k-th maximum: any value that between k and cap maxima reach
+// is valid (a looser one flags more scores).
+hipError_t launch_theta(const BatchPlan& p, int64_t B, int k, const BatchScratch& w, hipStream_t stream) {
   const int cap = k + max(8, k / 4);
   const dim3 tg((unsigned)((B + 3) / 4)), tb(256);
   const int te = (p.ns_tiles + kWave - 1) / kWave;
@@ -671,7 +884,105 @@ hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, in
     hipLaunchKernelGGL(theta_kernel<24>, tg, tb, 0, stream, w.tmax, p.ns_tiles, B, k, cap, w.theta);
   else
     hipLaunchKernelGGL(theta_kernel<32>, tg, tb, 0, stream, w.tmax, p.ns_tiles, B, k, cap, w.theta);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------- short-K strip pass
+constexpr int kStripMaxK = 256;
+constexpr int64_t kStripMinB = 256;
+constexpr int kStripBN = 256;   // draft rows per block (batch tile)
+
+int num_cus() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+    return cus;
+  }();
+  return n;
+}
+
+template <int BN, int KT>
+size_t strip_lds_bytes() {
+  return size_t(BN) * KT * 4 * sizeof(u32x4);
+}
+
+// Blocks of this kernel resident on the whole GPU at once.
+template <int BN, int KT, int MODE>
+int strip_slots() {
+  static const int slots = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, strip_sel_kernel<BN, KT, MODE>, kGemmThreads,
+                                                     strip_lds_bytes<BN, KT>()) != hipSuccess ||
+        nb < 1)
+      nb = 1;
+    return nb * num_cus();
+  }();
+  return slots;
+}
+
+// Strip groups G: the grid is G x NT persistent blocks. With several batch
+// tiles G is a multiple of 8 (the XCD mapping); with one, the strips are
+// spread evenly over at most `slots` blocks.
+int strip_groups(int nstrips, int NT, int slots) {
+  int G = slots / NT;
+  if (NT > 1) {
+    G = G / kXcds * kXcds;
+    if (G < kXcds) G = kXcds;
+    return G < nstrips ? G : nstrips;
+  }
+  if (G < 1) G = 1;
+  if (G > nstrips) G = nstrips;
+  const int per = (nstrips + G - 1) / G;
+  return (nstrips + per - 1) / per;
+}
+
+template <int BN, int KT>
+hipError_t allow_strip_lds() {
+  for (const void* f : {(const void*)strip_sel_kernel<BN, KT, kModeMax>,
+                        (const void*)strip_sel_kernel<BN, KT, kModeFilter>}) {
+    const hipError_t e =
+        hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)strip_lds_bytes<BN, KT>());
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int BN, int KT>
+hipError_t strip_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, int64_t V, int K, int64_t B, int k,
+                      const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream, Timing t) {
+  const int NT = (int)((B + BN - 1) / BN);
+  const size_t lds = strip_lds_bytes<BN, KT>();
+  const int NW = (int)(p.nvb * (kGemmBM / 64) * 4);   // 64-row mask slices
+  const int Gs = strip_groups(p.ns, NT, strip_slots<BN, KT, kModeMax>());
+  hipLaunchKernelGGL((strip_sel_kernel<BN, KT, kModeMax>), dim3((unsigned)(Gs * NT)), dim3(kGemmThreads), lds,
+                     stream, M, X, V, K, B, p.ns, p.stride, Gs, w.tmax, p.ns_tiles, nullptr, nullptr, 0, nullptr, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = launch_theta(p, B, k, w, stream)) != hipSuccess) return e;
+  const int nvb = (int)p.nvb;
+  const int Gm = strip_groups(nvb, NT, strip_slots<BN, KT, kModeFilter>());
+  LRH_LAUNCH(t, (strip_sel_kernel<BN, KT, kModeFilter>), dim3((unsigned)(Gm * NT)), dim3(kGemmThreads), lds, stream,
+             M, X, V, K, B, nvb, 1, Gm, nullptr, 0, w.theta, w.S, p.ldS, w.mask, NW);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(collect_kernel<64>, dim3((unsigned)B), dim3(kGemmThreads), 0, stream, w.mask, NW, w.S, p.ldS,
+                     B, k, idx, score);
+  return hipGetLastError();
+}
+
+template <int KT>
+hipError_t allow_strip_lds_k() {
+  return allow_strip_lds<kStripBN, KT>();
+}
+
+template <class C>
+hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, int64_t V, int K, int64_t B, int k,
+                    const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream, Timing t) {
+  hipError_t e = run_gemm<C>(kModeMax, M, X, V, K, B, p.ns, p.stride, w.tmax, p.ns_tiles, nullptr, nullptr, 0,
+                             nullptr, 0, stream);
+  if (e != hipSuccess) return e;
+  if ((e = launch_theta(p, B, k, w, stream)) != hipSuccess) return e;
   e = run_gemm<C>(kModeFilter, M, X, V, K, B, (int)p.nvb, 1, nullptr, 0, w.theta, w.S, p.ldS, w.mask, p.NW,
                   stream, t);
   if (e != hipSuccess) return e;
@@ -689,6 +1000,9 @@ hipError_t batch_init() {
   if (e == hipSuccess) e = allow_lds<CfgBig>();
   if (e == hipSuccess) e = allow_lds<CfgNarrow>();
   if (e == hipSuccess) e = allow_lds<CfgDown>();
+  if (e == hipSuccess) e = allow_strip_lds_k<2>();
+  if (e == hipSuccess) e = allow_strip_lds_k<4>();
+  if (e == hipSuccess) e = allow_strip_lds_k<8>();
   return e;
 }
 
@@ -733,6 +1047,7 @@ BatchScratch batch_scratch(void* base, int64_t V, int64_t B_max) {
   w.mask = reinterpret_cast<uint32_t*>(p);
   p += a(size_t(B_max) * size_t(nvb) * (kGemmBM / CfgNarrow::TM) * 4 * 4);
   w.S = reinterpret_cast<float*>(p);
+  w.S_bytes = size_t(B_max) * size_t(nvb) * kGemmBM * 4;
   return w;
 }
 
@@ -741,6 +1056,13 @@ hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, i
   const BatchPlan p = plan_batch(V, B, k);
   const uint16_t* m = static_cast<const uint16_t*>(M);
   const uint16_t* x = static_cast<const uint16_t*>(X);
+  // The strip kernel pays off once several batch tiles share each strip
+  // through L2; a single tile of rows streams M faster on the staged kernel.
+  if (K <= kStripMaxK && B > kStripMinB) {
+    if (K <= 64) return strip_pass<kStripBN, 2>(p, m, x, V, K, B, k, w, idx, score, stream, t);
+    if (K <= 128) return strip_pass<kStripBN, 4>(p, m, x, V, K, B, k, w, idx, score, stream, t);
+    return strip_pass<kStripBN, 8>(p, m, x, V, K, B, k, w, idx, score, stream, t);
+  }
   if (B <= 64) return run_pass<CfgNarrow>(p, m, x, V, K, B, k, w, idx, score, stream, t);
   if (B <= 128) return run_pass<CfgWide>(p, m, x, V, K, B, k, w, idx, score, stream, t);
   static_assert(CfgBig::TM == CfgWide::TM, "one mask layout above 64 rows");

@@ -106,6 +106,63 @@ __global__ void __launch_bounds__(NW * 64) down_mfma_kernel(const T* __restrict_
   }
 }
 
+// ------------------------------------------- split-K down-projection
+// For row batches the down-projection has few 16x16 output tiles (r/16 x
+// B/16) and a long K = d, so it is split over K across blocks: wave w of
+// block (x, y, kz) takes columns [(4 kz + w) * 128, +128) of its tile, the
+// four waves add up in LDS, and wave 0 writes the fp32 partial tile to
+// part[kz][b][j]. down_reduce_kernel then adds the partials of every z
+// component in kz order (a fixed order, so repeated calls agree bit for
+// bit) and rounds the sum to bf16.
+constexpr int kDownChunk = 128;   // K columns per wave
+
+__global__ void __launch_bounds__(256) down_split_kernel(const uint16_t* __restrict__ Q,
+                                                         const uint16_t* __restrict__ H, int r, int d, int64_t B,
+                                                         float* __restrict__ part) {
+  __shared__ f32x4 red[4][kWave];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, g = lane >> 4;
+  const int j0 = blockIdx.x * kTile;
+  const int64_t b0 = (int64_t)blockIdx.y * kTile;
+  const int kz = blockIdx.z;
+  const int qrow = j0 + col;
+  const int64_t hrow = b0 + col;
+  const bool q_ok = qrow < r, h_ok = hrow < B;
+  const int kb = min(d, (kz * 4 + wave) * kDownChunk), ke = min(d, kb + kDownChunk);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (ke > kb)
+    acc = tile_dot_unrolled<uint16_t>(Q + (int64_t)(q_ok ? qrow : 0) * d + kb, q_ok,
+                                      H + (h_ok ? hrow : 0) * (int64_t)d + kb, h_ok, ke - kb, acc);
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && h_ok) {
+    const f32x4 sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = j0 + 4 * g + q;
+      if (j < r) part[((int64_t)kz * B + hrow) * r + j] = sum[q];
+    }
+  }
+}
+
+// Z[i] = bf16(sum over kz of part[kz][i]) for the n = B * r components.
+__global__ void __launch_bounds__(256) down_reduce_kernel(const float* __restrict__ part, int S, int64_t n,
+                                                          uint16_t* __restrict__ Z) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  int kz = 0;
+  for (; kz + 8 <= S; kz += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(kz + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; kz < S; ++kz) s += part[(int64_t)kz * n + i];
+  Z[i] = f32_to_bf16(s);
+}
+
 // -------------------------------------------------- score pass + selection
 // Per wave and per column (draft row) of its tile: a sorted list of the best
 // 64 seen so far and a buffer of candidates that beat the column's k-th.
@@ -274,6 +331,22 @@ hipError_t launch_down(int dtype, const void* Q, const void* H, int r, int d, in
   else
     LRH_DISPATCH(dtype, hipLaunchKernelGGL((down_mfma_kernel<T, 4>), grid, dim3(4 * 64), 0, stream, (const T*)Q,
                                            (const T*)H, r, d, B, (T*)Z));
+  return hipGetLastError();
+}
+
+int down_split_parts(int d) { return ((d + kDownChunk - 1) / kDownChunk + 3) / 4; }
+
+hipError_t launch_down_split(const void* Q, const void* H, int r, int d, int64_t B, void* Z, float* part,
+                             hipStream_t stream) {
+  const int S = down_split_parts(d);
+  const dim3 grid((r + kTile - 1) / kTile, (unsigned)((B + kTile - 1) / kTile), (unsigned)S);
+  hipLaunchKernelGGL(down_split_kernel, grid, dim3(256), 0, stream, (const uint16_t*)Q, (const uint16_t*)H, r, d, B,
+                     part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = B * r;
+  hipLaunchKernelGGL(down_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, part, S, n,
+                     (uint16_t*)Z);
   return hipGetLastError();
 }
 

@@ -57,6 +57,12 @@ int plan_vsplit(int64_t B, int64_t V);
 // z = round(Q . h) for B rows: Z is B x r in the weight dtype.
 hipError_t launch_down(int dtype, const void* Q, const void* H, int r, int d, int64_t B,
                        void* Z, hipStream_t stream);
+// The same for bf16 row batches, split over K across blocks: fp32 partial
+// sums (down_split_parts(d) x B x r) in `part`, then a reduction in a fixed
+// order and the rounding to bf16.
+int down_split_parts(int d);
+hipError_t launch_down_split(const void* Q, const void* H, int r, int d, int64_t B, void* Z, float* part,
+                             hipStream_t stream);
 
 // Per-slice candidate lists of "M . x" for B rows: M is V x K (P or W),
 // X is B x K (z or h). Writes part_s / part_i: [B][k][n_vsplit].
@@ -88,6 +94,7 @@ struct BatchScratch {
   float* theta;     // B_max per-row bounds
   uint32_t* mask;   // B_max x NW flags
   float* S;         // B_max x ldS sparse scores
+  size_t S_bytes;
 };
 size_t batch_scratch_bytes(int64_t V, int64_t B_max);
 BatchScratch batch_scratch(void* base, int64_t V, int64_t B_max);

@@ -151,8 +151,13 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   const bool streaming = lrh::small_path(h->dtype, B, h->r, h->V);
   if (!streaming && lrh::batch_path(h->dtype, B)) {
     // many rows: the down-projection is a GEMM worth the pipelined kernel
+    // The sparse score array is written only later in the call, so the
+    // split down-projection keeps its partial sums there when they fit.
+    const size_t part_bytes = size_t(lrh::down_split_parts((int)h->d)) * size_t(B) * size_t(h->r) * 4;
     if (B >= kDownGemmRows)
       LRH_HIP(lrh::launch_down_gemm(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
+    else if (part_bytes <= h->bw.S_bytes)
+      LRH_HIP(lrh::launch_down_split(h->Q, H, (int)h->r, (int)h->d, B, h->z, h->bw.S, s), "down-projection launch");
     else
       LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
     LRH_HIP(lrh::launch_batch_select(h->P, h->z, h->V, (int)h->r, B, k, h->bw, idx, score, s, timing(h)),

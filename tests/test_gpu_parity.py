@@ -132,6 +132,8 @@ def test_streaming_path_shapes(V, d, r, B, k):
     (257, 64, 16, 9, 9),         # two vocabulary blocks, the second holding one row
     (3000, 200, 72, 300, 16),    # z on the GEMM kernel: r = 64 + 8, d = 3 * 64 + 8, ragged row tile
     (5000, 512, 256, 512, 64),   # z on the GEMM kernel, full tiles
+    (40000, 256, 256, 600, 64),  # strip kernel: three batch tiles, strip groups on the XCDs, ragged last strip
+    (7000, 5128, 64, 100, 32),   # split down-projection: 11 K parts, the last one 8 columns wide
 ])
 def test_batch_path_shapes(V, d, r, B, k):
     inp = gen.make_custom(V, d, r, B, "bf16", seed=V + B)
