@@ -40,10 +40,14 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense matrix peaks
 MALL_BYTES = 256 << 20
 BENCH_CONFIG = 2
-KERNEL_SOURCES = ["rank_lm_head_amd/csrc/kernels_small.hip", "rank_lm_head_amd/csrc/kernels_mfma.hip",
-                  "rank_lm_head_amd/csrc/kernels_gemm.hip",
-                  "rank_lm_head_amd/csrc/kernels_merge.hip", "rank_lm_head_amd/csrc/topk.h",
-                  "rank_lm_head_amd/csrc/device.h"]
+_CSRC = "rank_lm_head_amd/csrc/"
+# The sources each measured kernel is built from: its committed HBM counters
+# stay valid while these are unchanged.
+KERNEL_SOURCES = {
+    name: [_CSRC + f for f in (src, "topk.h", "device.h", "launch.h")]
+    for name, src in (("select_short_kernel", "kernels_small.hip"), ("select_mfma_kernel", "kernels_mfma.hip"),
+                      ("gemm_sel_kernel", "kernels_gemm.hip"), ("strip_sel_kernel", "kernels_gemm.hip"))
+}
 
 
 def parse():
@@ -94,9 +98,9 @@ class Hip:
         self.lib.hipEventDestroy(ev)
 
 
-def kernel_hash() -> str:
+def kernel_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -113,7 +117,7 @@ def traffic_from_profiles(kernel: str, workload: str):
         rec = json.load(open(path))[workload][kernel]
     except Exception:
         return None
-    if rec.get("kernel_hash") != kernel_hash():
+    if kernel not in KERNEL_SOURCES or rec.get("kernel_hash") != kernel_hash(kernel):
         return None
     return float(rec["bytes_per_launch"])
 
@@ -449,7 +453,9 @@ def main() -> int:
     sel_flops = 2.0 * cfg.B * cfg.V * cfg.r
     small = cfg.dtype == "bf16" and cfg.B <= 8 and cfg.r in (8, 16, 32, 64, 128, 256, 512)
     batch = cfg.dtype == "bf16" and cfg.B > 4 and not small
-    if batch:
+    if batch and cfg.r <= 256 and cfg.B > 256:
+        sel_kernel, what = "strip_sel_kernel", "main pass: scores of all rows, flagged above the sampled bound"
+    elif batch:
         sel_kernel, what = "gemm_sel_kernel", "main GEMM pass: scores of all rows, flagged above the sampled bound"
     elif small:
         sel_kernel, what = "select_short_kernel", "score pass + per-slice top-k"
