@@ -451,7 +451,7 @@ def main() -> int:
     # bound by whichever of HBM and MFMA its arithmetic intensity points to.
     sel_bytes = cfg.V * cfg.r * s + cfg.B * cfg.r * s
     sel_flops = 2.0 * cfg.B * cfg.V * cfg.r
-    small = cfg.dtype == "bf16" and cfg.B <= 8 and cfg.r in (8, 16, 32, 64, 128, 256, 512)
+    small = cfg.dtype == "bf16" and cfg.B <= (4 if cfg.r >= 512 else 8) and cfg.r in (8, 16, 32, 64, 128, 256, 512)
     batch = cfg.dtype == "bf16" and cfg.B > 4 and not small
     if batch and cfg.r <= 256 and cfg.B > 256:
         sel_kernel, what = "strip_sel_kernel", "main pass: scores of all rows, flagged above the sampled bound"

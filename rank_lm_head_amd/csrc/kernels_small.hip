@@ -291,7 +291,9 @@ int small_blocks(int64_t V) {
 }
 
 bool small_path(int dtype, int64_t B, int64_t K_lowrank, int64_t V) {
-  if (dtype != 0 || B > kSmallB) return false;
+  // rank-512 rows are long enough that from five rows on the matrix-core
+  // path is faster (measured: 77 against 107 us per call for eight rows)
+  if (dtype != 0 || B > (K_lowrank >= 512 ? kLongB : kSmallB)) return false;
   if (V > (int64_t)kMaxSmallBlocks * kBlockRows) return false;   // rows per block
   return K_lowrank >= 8 && K_lowrank <= 512 && (K_lowrank & (K_lowrank - 1)) == 0;
 }

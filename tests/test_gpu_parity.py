@@ -107,7 +107,7 @@ def test_small_heads(dt, V, d, r, B, k):
     (777, 64, 32, 6, 5),
     (300, 1032, 8, 7, 3),        # seven rows, r = 8, d not a multiple of 512
     (9000, 8200, 64, 8, 16),     # eight rows with d beyond the streaming down-projection
-    (30000, 5120, 512, 8, 64),   # eight rows at the drafter head's d, r at its maximum
+    (30000, 5120, 512, 4, 64),   # four rows at the drafter head's d, r at its maximum
     (200000, 64, 32, 8, 16),     # 391 rows per slice: the deepest score buffer
 ])
 def test_streaming_path_shapes(V, d, r, B, k):
@@ -134,6 +134,7 @@ def test_streaming_path_shapes(V, d, r, B, k):
     (5000, 512, 256, 512, 64),   # z on the GEMM kernel, full tiles
     (40000, 256, 256, 600, 64),  # strip kernel: three batch tiles, strip groups on the XCDs, ragged last strip
     (7000, 5128, 64, 100, 32),   # split down-projection: 11 K parts, the last one 8 columns wide
+    (30000, 5120, 512, 8, 64),   # eight rows at r = 512 take the matrix-core path
 ])
 def test_batch_path_shapes(V, d, r, B, k):
     inp = gen.make_custom(V, d, r, B, "bf16", seed=V + B)
