@@ -487,7 +487,7 @@ __device__ __forceinline__ void collect_rounds(CollectWave& m, const uint32_t* _
 }
 
 
-template <int TM>
+template <int TM, int T4>
 __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* __restrict__ mask, int NW,
                                                                 const float* __restrict__ S, int64_t ldS, int64_t B,
                                                                 int k, int32_t* __restrict__ idx,
@@ -501,8 +501,8 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
   if (threadIdx.x == 0) n_flag = 0;
   __syncthreads();
   // wave w takes the 16-byte word groups q = w * per + [0, per), in rounds of
-  // T4 per lane
-  constexpr int T4 = 4;
+  // T4 per lane (T4 = 12: one round for a 151936-token row, its loads all in
+  // flight; T4 = 4 for large batches, where more blocks per CU pay off)
   const int nq = (NW + 3) / 4;
   const int per = (nq + 3) / 4;
   const int q0 = wave * per, q1 = min(nq, q0 + per);
@@ -521,7 +521,7 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
     for (int t = 0; t < T4; ++t) cnt += __popc(wd[t][0]) + __popc(wd[t][1]) + __popc(wd[t][2]) + __popc(wd[t][3]);
     int before = 0, total = 0;
 #pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {   // at most 4 * T4 * 32 = 512 flags per lane
+    for (int bit = 0; bit < 8; ++bit) {   // counts from 256 on take the rounds below
       const unsigned long long plane = __ballot((cnt >> bit) & 1);
       before += lanes_below(plane) << bit;
       total += __popcll(plane) << bit;
@@ -869,6 +869,19 @@ hipError_t run_gemm(int mode, const uint16_t* M, const uint16_t* X, int64_t V, i
   return hipGetLastError();
 }
 
+// One block per row; the width of the mask rounds by batch size.
+template <int TM>
+hipError_t launch_collect(const uint32_t* mask, int NW, const float* S, int64_t ldS, int64_t B, int k, int32_t* idx,
+                          float* score, hipStream_t stream) {
+  if (B <= 1024)
+    hipLaunchKernelGGL((collect_kernel<TM, 12>), dim3((unsigned)B), dim3(kGemmThreads), 0, stream, mask, NW, S, ldS,
+                       B, k, idx, score);
+  else
+    hipLaunchKernelGGL((collect_kernel<TM, 4>), dim3((unsigned)B), dim3(kGemmThreads), 0, stream, mask, NW, S, ldS,
+                       B, k, idx, score);
+  return hipGetLastError();
+}
+
 // theta of every row from the sample pass's tile maxima. The bound need not
 // be the exact k-th maximum: any value that between k and cap maxima reach
 // is valid (a looser one flags more scores).
@@ -966,9 +979,7 @@ hipError_t strip_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, 
   LRH_LAUNCH(t, (strip_sel_kernel<BN, KT, kModeFilter>), dim3((unsigned)(Gm * NT)), dim3(kGemmThreads), lds, stream,
              M, X, V, K, B, nvb, 1, Gm, nullptr, 0, w.theta, w.S, p.ldS, w.mask, NW);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(collect_kernel<64>, dim3((unsigned)B), dim3(kGemmThreads), 0, stream, w.mask, NW, w.S, p.ldS,
-                     B, k, idx, score);
-  return hipGetLastError();
+  return launch_collect<64>(w.mask, NW, w.S, p.ldS, B, k, idx, score, stream);
 }
 
 template <int KT>
@@ -986,9 +997,7 @@ hipError_t run_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, in
   e = run_gemm<C>(kModeFilter, M, X, V, K, B, (int)p.nvb, 1, nullptr, 0, w.theta, w.S, p.ldS, w.mask, p.NW,
                   stream, t);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(collect_kernel<C::TM>, dim3((unsigned)B), dim3(kGemmThreads), 0, stream, w.mask,
-                     p.NW, w.S, p.ldS, B, k, idx, score);
-  return hipGetLastError();
+  return launch_collect<C::TM>(w.mask, p.NW, w.S, p.ldS, B, k, idx, score, stream);
 }
 
 }  // namespace
