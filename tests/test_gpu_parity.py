@@ -135,6 +135,8 @@ def test_streaming_path_shapes(V, d, r, B, k):
     (40000, 256, 256, 600, 64),  # strip kernel: three batch tiles, strip groups on the XCDs, ragged last strip
     (7000, 5128, 64, 100, 32),   # split down-projection: 11 K parts, the last one 8 columns wide
     (30000, 5120, 512, 8, 64),   # eight rows at r = 512 take the matrix-core path
+    (100, 64, 16, 300, 8),       # strip kernel: one partial strip (V < 256), two batch tiles
+    (3000, 64, 8, 300, 16),      # strip kernel at r = 8: K steps mostly past the row, zero z chunks
 ])
 def test_batch_path_shapes(V, d, r, B, k):
     inp = gen.make_custom(V, d, r, B, "bf16", seed=V + B)
