@@ -407,6 +407,10 @@ def main() -> int:
     t_hot = timed_graph_replays(torch, g_hot, K // R)
     us_cold = t_cold / K * 1e6
     us_hot = t_hot / K * 1e6
+    # spread of the cold figure: 7 more trials of about K/7 calls each,
+    # outside the timed region above
+    n_tr = max(1, (K // 7) // R)
+    trials = sorted(timed_graph_replays(torch, g_cold, n_tr) / (n_tr * R) * 1e6 for _ in range(7))
     sel_s = event_timed(torch, hip, heads, cold, min(K, 1400))
 
     # distinct W rows gathered by the last call of the cold loop
@@ -495,6 +499,8 @@ def main() -> int:
                    "cache": f"cold: {R} rotating (Q, P, h) sets, {R * lowrank_bytes / 2**20:.0f} MiB",
                    "launch": "HIP graph replay"},
         "us_per_call": us_cold,
+        "us_per_call_trials": {"n": 7, "calls_each": n_tr * R, "median": trials[3], "min": trials[0],
+                               "max": trials[-1]},
         "us_per_call_hot": us_hot,
         "call_hbm_frac": call_bytes / (us_cold * 1e-6) / (HBM_PEAK_GBS * 1e9),
         "call_bytes": call_bytes,
