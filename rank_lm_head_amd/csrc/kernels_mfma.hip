@@ -150,16 +150,16 @@ __global__ void __launch_bounds__(256) down_reduce_kernel(const float* __restric
                                                           uint16_t* __restrict__ Z) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
+  // up to 16 parts per round, all loads in flight (clamped addresses), added
+  // in kz order
   float s = 0.f;
-  int kz = 0;
-  for (; kz + 8 <= S; kz += 8) {
-    float v[8];
+  for (int kz = 0; kz < S; kz += 16) {
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(kz + u) * n + i];
+    for (int u = 0; u < 16; ++u) v[u] = part[(int64_t)min(kz + u, S - 1) * n + i];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
+    for (int u = 0; u < 16; ++u) s = kz + u < S ? s + v[u] : s;
   }
-  for (; kz < S; ++kz) s += part[(int64_t)kz * n + i];
   Z[i] = f32_to_bf16(s);
 }
 
