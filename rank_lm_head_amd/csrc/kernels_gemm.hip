@@ -8,7 +8,7 @@
 // S is B x V and never stored whole. The selection uses a per-row bound:
 //
 //   1. Sample pass. The same GEMM over every `stride`-th block of vocabulary
-//      rows keeps, per draft row, the maximum of each 16-row tile. The k-th
+//      rows keeps, per draft row, the maximum of each 32-row tile. The k-th
 //      largest of those maxima, theta_b, is reached by at least k distinct
 //      scores of row b (one per tile), so it is a lower bound of the row's
 //      k-th best score.
@@ -138,7 +138,7 @@ __device__ __forceinline__ float fmax_lanes(float m) {
 // Grid: 1-D, round_up(nvb, 8) * ceil(B / BN) blocks (see the XCD mapping
 // above); nvb vocabulary blocks of BM rows, the s-th being block s * stride.
 //  kModeMax:    aux_f = tile maxima, row n at aux_f + n * ns_tiles, tile
-//               index s * (BM/16) + (16-row tile within the block).
+//               index s * (BM/32) + (32-row tile within the block).
 //  kModeFilter: theta = per-row bound; S = sparse scores (row n at
 //               S + n * ldS); mask = per row NW words, word
 //               ((vb * WM + wm) * 4 + g) holds bit (i * 4 + q) for vocabulary
@@ -240,17 +240,21 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
   // --------------------------------------------------------------- epilogue
   const int64_t vrow = m0 + wm * C::TM + 4 * g;   // + i * 16 + q
   if constexpr (MODE == kModeMax) {
+    // the maximum of each 32-row tile (two 16-row tiles of the wave)
+    static_assert(C::FM % 2 == 0, "whole 32-row tiles per wave");
 #pragma unroll
     for (int jn = 0; jn < C::FN; ++jn) {
       const int64_t n = n0 + wn * C::TN + jn * 16 + col;
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i) {
+      for (int i2 = 0; i2 < C::FM / 2; ++i2) {
         float m = neg_inf();
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (vrow + i * 16 + q < V) m = fmaxf(m, acc[i][jn][q]);
+        for (int i = 2 * i2; i < 2 * i2 + 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (vrow + i * 16 + q < V) m = fmaxf(m, acc[i][jn][q]);
         m = fmax_lanes(m);
-        if (g == 0 && n < B) aux_f[n * ns_tiles + vb_local * (C::BM / 16) + wm * C::FM + i] = m;
+        if (g == 0 && n < B) aux_f[n * ns_tiles + vb_local * (C::BM / 32) + wm * (C::FM / 2) + i2] = m;
       }
     }
   } else if constexpr (MODE == kModeStore) {
@@ -615,8 +619,8 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
 // 16x16 tile of scores comes out of the same MFMA sequence in both, and the
 // bound of the sample pass holds bit for bit in the main pass.
 // Strip s covers vocabulary rows [s * stride * 256, s * stride * 256 + 256).
-//  kModeMax:    tile maxima, row n at aux_f + n * ns_tiles, index s * 16 +
-//               w * 4 + i for the 16-row tile i of wave w;
+//  kModeMax:    tile maxima, row n at aux_f + n * ns_tiles, index s * 8 +
+//               w * 2 + i2 for the 32-row tile i2 of wave w;
 //  kModeFilter: per-row bound theta; flagged scores into S (row n at
 //               S + n * ldS) and one mask word per (row, 64-row slice,
 //               lane group): word (vb * 4 + w) * 4 + g holds bit i * 4 + q
@@ -769,13 +773,15 @@ __global__ void __launch_bounds__(kGemmThreads) strip_sel_kernel(
       for (int jn = 0; jn < NF; ++jn) {
         const int64_t n = n0 + jn * 16 + col;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i2 = 0; i2 < 2; ++i2) {   // the maximum of each 32-row tile
           float m = neg_inf();
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (vrow + i * 16 + q < V) m = fmaxf(m, acc[i][jn][q]);
+          for (int i = 2 * i2; i < 2 * i2 + 2; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (vrow + i * 16 + q < V) m = fmaxf(m, acc[i][jn][q]);
           m = fmax_lanes(m);
-          if (g == 0 && n < B) aux_f[n * ns_tiles + s * 16 + wave * 4 + i] = m;
+          if (g == 0 && n < B) aux_f[n * ns_tiles + s * 8 + wave * 2 + i2] = m;
         }
       }
     } else {
@@ -1026,7 +1032,7 @@ BatchPlan plan_batch(int64_t V, int64_t B, int k) {
   p.nvb = vblocks(V);
   p.stride = sample_stride(V, k);
   p.ns = (int)((p.nvb + p.stride - 1) / p.stride);
-  p.ns_tiles = p.ns * (kGemmBM / 16);
+  p.ns_tiles = p.ns * (kGemmBM / 32);
   p.ldS = p.nvb * kGemmBM;
   const int tm = B <= 64 ? CfgNarrow::TM : CfgWide::TM;
   p.NW = (int)(p.nvb * (kGemmBM / tm) * 4);
