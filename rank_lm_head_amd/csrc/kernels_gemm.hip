@@ -597,10 +597,9 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
 }
 
 // ------------------------------------------------ short-K vocabulary pass
-// For the low-rank scores K = r <= 256, so a lane's share of a 64-row
-// operand tile over the whole K fits in registers (KT * 4 16-byte
-// fragments). A block then keeps its BN draft rows of X (= z) in LDS for its
-// whole life and streams strips of 256 vocabulary rows of M past them:
+// For the low-rank scores K = r <= 256 is short: a block keeps its BN draft
+// rows of X (= z, BN x K) in LDS for its whole life and streams strips of
+// 256 vocabulary rows of M past them:
 //  - wave w owns rows [64 w, 64 w + 64) of a strip (four 16-row tiles), and
 //    reads their K columns straight from global memory into the A operands
 //    of the matrix cores;
