@@ -328,10 +328,15 @@ def test_ties_inside_one_slice_go_to_the_lower_ids(B):
     assert not errs, errs[:5]
 
 
-def test_repeat_calls_and_poisoned_workspace_are_bitwise_stable():
-    inp = gen.make_custom(20000, 512, 128, 40, "bf16", seed=6)
+@pytest.mark.parametrize("V,d,r,B", [
+    (20000, 512, 128, 40),   # staged GEMM passes, split down-projection
+    (20000, 512, 128, 300),  # strip kernel (two batch tiles), split down-projection in the score scratch
+])
+def test_repeat_calls_and_poisoned_workspace_are_bitwise_stable(V, d, r, B):
+    inp = gen.make_custom(V, d, r, B, "bf16", seed=6)
     t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
-    head = lr.Head(t["Q"], t["P"], t["W"], B_max=40, k_max=64)
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=64)
+    say(f"[run] poisoned workspace V={V} d={d} r={r} B={B}")
     ref = [np_(x) for x in head.draft(t["H"], 64)]
     for trial in range(5):
         head.workspace.fill_(0xFF if trial % 2 else 0x7F)     # NaN / large garbage
