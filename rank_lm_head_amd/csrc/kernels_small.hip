@@ -10,65 +10,21 @@
 // the memory side: every wave load is 64 lanes x 16 contiguous bytes, and
 // each wave keeps several loads in flight.
 //
-//   down_small_kernel   z = Q . h: one wave per row of Q
 //   select_short_kernel s = P . z with the fused k-best of each block's
 //                       slice, for r <= 512 (a power of two)
 //   select_long_kernel  the same for rows longer than one wave load (the
 //                       full-head baseline, W . h)
-// The slice lists are merged, and the winners rescored, by merge_kernel.
+// z = Q . h comes from down_wide_kernel (kernels_b1.hip). The slice lists are
+// merged, and the winners rescored, by merge_kernel; one-row calls take the
+// fused pass of kernels_b1.hip instead.
 #include "launch.h"
+#include "stream.h"
 #include "topk.h"
 
 namespace lrh {
 
 constexpr int kWavesSmall = 4;
 constexpr int kSmallThreads = kWavesSmall * kWave;
-
-// ------------------------------------------------------------ z = Q . h
-// Wave w of block x computes z[b][j] for j = 4x + w and every row b < B.
-// A row of Q is NL wave loads of 1 KiB (d <= NL * 512); all of them and the
-// matching chunks of h are issued before the products. Loads past d read a
-// clamped, valid address and are zeroed afterwards, so no load is predicated.
-// The rows of h go in chunks of up to four (their loads for eight rows would
-// not fit in registers next to the row of Q); later chunks hit in L2.
-template <int NB, int NL>
-__global__ void __launch_bounds__(kSmallThreads) down_small_kernel(const uint16_t* __restrict__ Q,
-                                                                   const uint16_t* __restrict__ H, int r,
-                                                                   int d, int B, uint16_t* __restrict__ Z) {
-  constexpr int CH = NB < 4 ? NB : 4;
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int j = blockIdx.x * kWavesSmall + wave;
-  if (j >= r) return;
-  const uint16_t* q = Q + (int64_t)j * d;
-  u32x4 qv[NL];
-  int cols[NL];
-#pragma unroll
-  for (int t = 0; t < NL; ++t) {
-    const int c = (t * kWave + lane) * 8;
-    cols[t] = c < d ? c : d - 8;
-    qv[t] = load16(q + cols[t]);
-  }
-#pragma unroll
-  for (int b0 = 0; b0 < NB; b0 += CH) {
-    if (b0 >= B) break;
-    u32x4 hv[CH][NL];
-#pragma unroll
-    for (int t = 0; t < NL; ++t)
-#pragma unroll
-      for (int b = 0; b < CH; ++b) hv[b][t] = load16(H + (int64_t)(b0 + b < B ? b0 + b : 0) * d + cols[t]);
-#pragma unroll
-    for (int b = 0; b < CH; ++b) {
-      float acc = 0.f;
-#pragma unroll
-      for (int t = 0; t < NL; ++t) {
-        const bool ok = (t * kWave + lane) * 8 < d;
-        acc = dot8_bf16(ok ? qv[t] : u32x4{0u, 0u, 0u, 0u}, hv[b][t], acc);
-      }
-      const float z = group_sum<kWave>(acc);
-      if (b0 + b < B && lane == 0) Z[(int64_t)(b0 + b) * r + j] = f32_to_bf16(z);
-    }
-  }
-}
 
 // ------------------------------------------------- shared tail of the pass
 // Each wave hands its per-row lists to LDS; wave b merges the four lists of
@@ -126,21 +82,8 @@ template <int K, int NB, int E>
 __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
     const uint16_t* __restrict__ M, const uint16_t* __restrict__ X, int64_t V, int B, int L,
     float* __restrict__ part_s, int* __restrict__ part_i, float* __restrict__ raw) {
-  constexpr int LPR = K / 8;
-  constexpr int RPL = kWave / LPR;
-  constexpr int U = 8;   // wave loads per group
-  constexpr int STEP = U * RPL;
-  static_assert(K % 8 == 0 && LPR <= kWave && (LPR & (LPR - 1)) == 0, "row length");
   __shared__ float sc[NB][E * kWave];
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int c = lane % LPR, sub = lane / LPR;
-
-  // z first (one load per row, unpredicated), widened only after the first
-  // group of P loads is issued
-  u32x4 zr[NB];
-  f32x8 zc[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) zr[b] = load16(X + (int64_t)(b < B ? b : 0) * K + 8 * c);
 
   // slice bounds V*x/n in 32 bits: this path keeps V*n below 2^27
   const int64_t nblk = gridDim.x;
@@ -148,56 +91,7 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
   const int64_t blo = v32 * blockIdx.x / n32, bhi = v32 * (blockIdx.x + 1) / n32;
   const int64_t wlo = blo + (bhi - blo) * wave / kWavesSmall;
   const int64_t whi = blo + (bhi - blo) * (wave + 1) / kWavesSmall;
-
-  // The wave's rows go in groups of STEP (U wave loads), two groups in
-  // flight: group g + 1 is issued before group g is used. The loop takes two
-  // groups per iteration with fixed buffers (no register copies, which would
-  // wait for the loads in flight); the last group prefetches nothing, so no
-  // load is outstanding after the pass. Rows past the wave's range are loaded
-  // from its last row (a valid address, so no load is predicated) and never
-  // kept (a wave without rows loads row 0).
-  const int64_t last = whi > 0 ? whi - 1 : 0;
-  const int ng = wlo < whi ? (int)((whi - wlo + STEP - 1) / STEP) : 0;
-  u32x4 buf0[U], buf1[U];
-  auto issue = [&](u32x4 (&buf)[U], int64_t base) {
-#pragma unroll
-    for (int t = 0; t < U; ++t) {
-      const int64_t row = base + t * RPL + sub;
-      buf[t] = load16(M + (row < last ? row : last) * K + 8 * c);
-    }
-  };
-  auto consume = [&](const u32x4 (&buf)[U], int64_t base) {
-#pragma unroll
-    for (int t = 0; t < U; ++t) {
-      const int64_t row = base + t * RPL + sub;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if (b >= B) break;
-        const float s = group_sum<LPR>(dot8_bf16(buf[t], zc[b], 0.f));
-        if (c == 0 && row < whi) sc[b][row - blo] = s;
-      }
-    }
-  };
-  issue(buf0, wlo);   // unconditional: a branch here would make the first use wait for every load
-  __builtin_amdgcn_sched_barrier(0);   // all of them before anything waits for z
-#pragma unroll
-  for (int b = 0; b < NB; ++b) zc[b] = widen8(b < B ? zr[b] : u32x4{0u, 0u, 0u, 0u});
-  int g = 0;
-  for (; g + 2 < ng; g += 2) {   // buf0 holds group g on entry
-    const int64_t base = wlo + (int64_t)g * STEP;
-    issue(buf1, base + STEP);
-    consume(buf0, base);
-    issue(buf0, base + 2 * STEP);
-    consume(buf1, base + STEP);
-  }
-  if (g + 1 < ng) {
-    const int64_t base = wlo + (int64_t)g * STEP;
-    issue(buf1, base + STEP);
-    consume(buf0, base);
-    consume(buf1, base + STEP);
-  } else if (g < ng) {
-    consume(buf0, wlo + (int64_t)g * STEP);
-  }
+  stream_scores<K, NB>(M, X, B, blo, wlo, whi, &sc[0][0], E * kWave);
   __syncthreads();
   const int nrows = (int)(bhi - blo);
   if (B < kWavesSmall) {
@@ -354,17 +248,6 @@ static int row_loads(int K) {
       __VA_ARGS__;                       \
     }                                    \
   } while (0)
-
-hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream) {
-  if (B < 1 || B > kSmallB) return hipErrorInvalidValue;
-  dim3 grid((r + kWavesSmall - 1) / kWavesSmall);
-  const int nl = row_loads(d);
-  if (nl < 0) return launch_down(0, Q, H, r, d, B, Z, stream);   // rows longer than 8192
-  LRH_NB_DISPATCH(B, LRH_NL_DISPATCH(nl, hipLaunchKernelGGL((down_small_kernel<NB, NL>), grid,
-                                                               dim3(kSmallThreads), 0, stream, (const uint16_t*)Q,
-                                                               (const uint16_t*)H, r, d, (int)B, (uint16_t*)Z)));
-  return hipGetLastError();
-}
 
 int small_list_len(int k) { return k < kSliceList ? k : kSliceList; }
 

@@ -37,8 +37,6 @@ int small_blocks(int64_t V);
 bool small_path(int dtype, int64_t B, int64_t K, int64_t V);
 bool small_long_path(int dtype, int64_t B, int64_t K, int64_t V);
 
-// z = round(Q . h) for B <= kSmallB rows.
-hipError_t launch_down_small(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream);
 // Streaming score pass: per block, the small_list_len(k) best of its slice
 // for each row, written depth-major (entry j of block x's list at
 // part_[row][j][x]), and every score to raw[row][v] (B x V).
@@ -48,6 +46,41 @@ hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, i
                                int* part_i, float* raw, hipStream_t stream, Timing t = {});
 hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
                               int* part_i, hipStream_t stream, Timing t = {});
+
+// ------------------------------------------------------- kernels_b1.hip
+// z = round(Q . h) for B <= kSmallB rows, one block per row of Q; block 0
+// also zeroes nsync completion counters (128 bytes apart) of the next pass.
+hipError_t launch_down_wide(const void* Q, const void* H, int r, int d, int64_t B, void* Z, uint32_t* sync,
+                            int nsync, hipStream_t stream);
+// The one-row call in one pass after the down-projection: score stream,
+// slice lists, the speculative logit of each slice's best entry, and the
+// merge with the remaining logits in the pass's last block.
+constexpr int kB1Counters = 9;   // completion counters the pass uses
+constexpr int kB1MaxLists = 512; // slice lists of the pass (blocks)
+constexpr int kB1MaxList = 4;    // entries per list
+int b1_blocks(int64_t V, int n_cu);
+bool b1_path(int dtype, int64_t B, int64_t K, int64_t V, int n_cu);
+int b1_list_len(int k);
+struct B1Args {
+  const void* P;
+  const void* Z;
+  int64_t V;
+  int K;             // rank r
+  int k;
+  int L;             // slice list length, min(4, k)
+  const void* W;     // with logits
+  const void* H;
+  int d;
+  uint64_t* keys;    // lists: candidate key of entry j of list x at [j * n + x]
+  float* lgs;        // and its exact logit
+  float* raw;        // V raw scores (read only when L < k)
+  uint32_t* sync;    // kB1Counters counters, zeroed by launch_down_wide
+  int n_cu;
+  int32_t* idx;
+  float* score;      // may be NULL
+  float* logits;     // NULL: candidates only
+};
+hipError_t launch_draft1(const B1Args& a, hipStream_t stream, Timing t = {});
 
 // ------------------------------------------------------ kernels_mfma.hip
 // Vocabulary slices of the matrix-core selection pass for B rows over V

@@ -29,6 +29,10 @@ struct lrhead_s {
   float* part_s;    // candidate lists: rows x slices x k_max
   int* part_i;
   float* raw;       // raw scores of the streaming path: min(B_max, 8) x V
+  uint64_t* b1_keys;  // one-row pass: slice lists (candidate keys)
+  float* b1_lgs;      // one-row pass: their speculative exact logits
+  uint32_t* sync;     // one-row pass: completion counters
+  int n_cu;           // compute units of the device
   bool batch;       // bf16 with B_max > 4: the GEMM path's scratch exists
   lrh::BatchScratch bw;
   hipEvent_t ev_before;  // optional events attached to the score pass: its start
@@ -61,7 +65,7 @@ size_t elem_bytes(int dtype) { return dtype == LRHEAD_BF16 ? 2 : 4; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t z, part_s, part_i, raw, batch, total;
+  size_t z, part_s, part_i, raw, b1_keys, b1_lgs, sync, batch, total;
 };
 
 // Most candidate lists any call with B <= B_max writes (B x slices), over
@@ -90,7 +94,10 @@ Layout layout(int dtype, int64_t V, int64_t r, int64_t B_max, int k_max) {
   // raw scores of the streaming path (bf16 heads, B <= kSmallB rows)
   const int64_t raw_rows = dtype == LRHEAD_BF16 ? (B_max < lrh::kSmallB ? B_max : lrh::kSmallB) : 0;
   L.raw = zb + 2 * lists;
-  L.batch = L.raw + align256(size_t(raw_rows) * size_t(V) * 4);
+  L.b1_keys = L.raw + align256(size_t(raw_rows) * size_t(V) * 4);
+  L.b1_lgs = L.b1_keys + align256(size_t(lrh::kB1MaxLists) * lrh::kB1MaxList * 8);
+  L.sync = L.b1_lgs + align256(size_t(lrh::kB1MaxLists) * lrh::kB1MaxList * 4);
+  L.batch = L.sync + align256(size_t(lrh::kB1Counters) * 128);
   L.total = L.batch;
   if (lrh::batch_path(dtype, B_max)) L.total += align256(lrh::batch_scratch_bytes(V, B_max));
   return L;
@@ -149,6 +156,32 @@ lrh::Timing timing(const lrhead_s* h) { return lrh::Timing{h->ev_before, h->ev_a
 // the slice lists; with `logits`, the merge also rescores the winners.
 int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, float* score, float* logits,
                  hipStream_t s) {
+  if (lrh::b1_path(h->dtype, B, h->r, h->V, h->n_cu)) {
+    // one row: the down-projection (which also resets the pass's counters),
+    // then a single pass that scores, selects, merges and rescores
+    LRH_HIP(lrh::launch_down_wide(h->Q, H, (int)h->r, (int)h->d, B, h->z, h->sync, lrh::kB1Counters, s),
+            "down-projection launch");
+    lrh::B1Args a;
+    a.P = h->P;
+    a.Z = h->z;
+    a.V = h->V;
+    a.K = (int)h->r;
+    a.k = k;
+    a.L = lrh::b1_list_len(k);
+    a.W = h->W;
+    a.H = H;
+    a.d = (int)h->d;
+    a.keys = h->b1_keys;
+    a.lgs = h->b1_lgs;
+    a.raw = h->raw;
+    a.sync = h->sync;
+    a.n_cu = h->n_cu;
+    a.idx = idx;
+    a.score = score;
+    a.logits = logits;
+    LRH_HIP(lrh::launch_draft1(a, s, timing(h)), "score/selection launch");
+    return LRHEAD_OK;
+  }
   const bool streaming = lrh::small_path(h->dtype, B, h->r, h->V);
   if (!streaming && lrh::batch_path(h->dtype, B)) {
     // many rows: the down-projection is a GEMM worth the pipelined kernel
@@ -173,7 +206,7 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   int n_lists, list_len = k;
   const float* raw = nullptr;
   if (streaming) {
-    LRH_HIP(lrh::launch_down_small(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
+    LRH_HIP(lrh::launch_down_wide(h->Q, H, (int)h->r, (int)h->d, B, h->z, nullptr, 0, s), "down-projection launch");
     LRH_HIP(lrh::launch_select_small(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, h->raw, s,
                                      timing(h)),
             "score/selection launch");
@@ -223,6 +256,8 @@ int lrhead_create(lrhead_t* out, int dtype, int64_t V, int64_t d, int64_t r, con
     return fail(LRHEAD_EDEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
 
   if (lrh::batch_path(dtype, B_max)) LRH_HIP(lrh::batch_init(), "GEMM kernel set-up");
+  int n_cu = 0;
+  LRH_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev), "hipDeviceGetAttribute");
 
   lrhead_s* h = new (std::nothrow) lrhead_s;
   if (!h) return fail(LRHEAD_EINVAL, "out of host memory");
@@ -242,6 +277,10 @@ int lrhead_create(lrhead_t* out, int dtype, int64_t V, int64_t d, int64_t r, con
   h->part_s = reinterpret_cast<float*>(h->ws + L.part_s);
   h->part_i = reinterpret_cast<int*>(h->ws + L.part_i);
   h->raw = reinterpret_cast<float*>(h->ws + L.raw);
+  h->b1_keys = reinterpret_cast<uint64_t*>(h->ws + L.b1_keys);
+  h->b1_lgs = reinterpret_cast<float*>(h->ws + L.b1_lgs);
+  h->sync = reinterpret_cast<uint32_t*>(h->ws + L.sync);
+  h->n_cu = n_cu;
   h->batch = lrh::batch_path(dtype, B_max);
   h->bw = h->batch ? lrh::batch_scratch(h->ws + L.batch, V, B_max) : lrh::BatchScratch{};
   h->ev_before = nullptr;

@@ -418,29 +418,35 @@ __device__ __forceinline__ void wave_topk_emit(const uint64_t (&key)[E], int k, 
 }
 
 // ------------------------------------------------- a few best by argmax
-// Wave-wide maximum of a 64-bit key: DPP inside rows of 16 lanes, then the
-// four row results by readlane.
-// The L best (L <= 64) of a slice's n <= E * 64 scores held in LDS (entry j
-// at sc[j], token id id0 + j), in candidate order, to out_s/out_i[r * stride]
-// for r < L; ranks past n get empty entries. Entry j = e * 64 + lane sits in
-// lane `lane` as element e, so within a lane a lower e is a lower id.
-// Each round takes the wave-wide maximum of the 32-bit score images (each
-// lane offers its best element, the lowest e among equal ones), then the
-// lanes holding it: almost always one, and otherwise the lowest id among
-// them (smallest e, then lowest lane). The winner's element is cleared.
+// The best entries of a slice's n <= E * 64 scores held in LDS (entry j at
+// sc[j], token id id0 + j), one per round, in candidate order. Entry
+// j = e * 64 + lane sits in lane `lane` as element e, so within a lane a
+// lower e is a lower id. Each round takes the wave-wide maximum of the
+// 32-bit score images (each lane offers its best element, the lowest e among
+// equal ones), then the lanes holding it: almost always one, and otherwise
+// the lowest id among them (smallest e, then lowest lane). The winner's
+// element is cleared; round r leaves the winner in lane r (my_s, my_i).
 template <int E>
-__device__ __forceinline__ void wave_top_few(const float* sc, int n, int id0, int L, float* __restrict__ out_s,
-                                             int* __restrict__ out_i, int64_t stride) {
-  const int lane = threadIdx.x & 63;
-  float v[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) v[e] = sc[min(e * kWave + lane, n - 1)];
+struct SliceTop {
   uint32_t h[E];   // 0 = empty (no finite score maps to 0)
+  float my_s;
+  int my_i;
+
+  __device__ __forceinline__ void load(const float* sc, int n) {
+    const int lane = threadIdx.x & 63;
+    float v[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) h[e] = e * kWave + lane < n ? order_key(v[e] + 0.0f) : 0u;
-  float my_s = neg_inf();
-  int my_i = kSentinelId;
-  for (int r = 0; r < L; ++r) {
+    for (int e = 0; e < E; ++e) v[e] = sc[min(e * kWave + lane, n - 1)];
+#pragma unroll
+    for (int e = 0; e < E; ++e) h[e] = e * kWave + lane < n ? order_key(v[e] + 0.0f) : 0u;
+    my_s = neg_inf();
+    my_i = kSentinelId;
+  }
+
+  // Round r; returns the winner's id (wave-uniform), or kSentinelId when
+  // the slice has no entries left.
+  __device__ __forceinline__ int round(int r, int id0) {
+    const int lane = threadIdx.x & 63;
     uint32_t best = h[0];
     int be = 0;
 #pragma unroll
@@ -450,7 +456,7 @@ __device__ __forceinline__ void wave_top_few(const float* sc, int n, int id0, in
       be = t ? e : be;
     }
     const uint32_t M = wave_max_u32(best);
-    if (M == 0) break;   // fewer than L entries
+    if (M == 0) return kSentinelId;
     unsigned long long mk = __ballot(best == M);
     if (mk & (mk - 1)) {   // equal scores in several lanes
       const uint32_t me = wave_min_u32(best == M ? (uint32_t)be : 0xFFu);
@@ -460,14 +466,29 @@ __device__ __forceinline__ void wave_top_few(const float* sc, int n, int id0, in
     const int we = __builtin_amdgcn_readlane(be, wl);
 #pragma unroll
     for (int e = 0; e < E; ++e) h[e] = (lane == wl && e == we) ? 0u : h[e];
+    const int id = id0 + we * kWave + wl;
     if (lane == r) {
       my_s = __uint_as_float(order_key_inv(M));
-      my_i = id0 + we * kWave + wl;
+      my_i = id;
     }
+    return id;
   }
+};
+
+// The L best (L <= 64) of a slice's n <= E * 64 scores held in LDS, in
+// candidate order, to out_s/out_i[r * stride] for r < L; ranks past n get
+// empty entries.
+template <int E>
+__device__ __forceinline__ void wave_top_few(const float* sc, int n, int id0, int L, float* __restrict__ out_s,
+                                             int* __restrict__ out_i, int64_t stride) {
+  const int lane = threadIdx.x & 63;
+  SliceTop<E> st;
+  st.load(sc, n);
+  for (int r = 0; r < L; ++r)
+    if (st.round(r, id0) == kSentinelId) break;   // fewer than L entries
   if (lane < L) {
-    out_s[lane * stride] = my_s;
-    out_i[lane * stride] = my_i;
+    out_s[lane * stride] = st.my_s;
+    out_i[lane * stride] = st.my_i;
   }
 }
 

@@ -266,14 +266,61 @@ def test_config_full_head_baseline(cid):
 
 # ------------------------------------------------------ invariants on the GPU
 
-def test_h_times_two_doubles_everything_bitwise():
-    inp = gen.make_custom(5000, 256, 64, 20, "bf16", seed=4)
+@pytest.mark.parametrize("B", [1, 8, 20])
+def test_h_times_two_doubles_everything_bitwise(B):
+    """h -> 2h is exact in bf16: z, scores and logits double bit for bit and
+    the ids stay (one-row pass, eight-row streaming path, row batch)."""
+    inp = gen.make_custom(5000, 256, 64, B, "bf16", seed=4)
     t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
-    head = lr.Head(t["Q"], t["P"], t["W"], B_max=20, k_max=32)
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=32)
     a = [np_(x) for x in head.draft(t["H"], 32)]
     b = [np_(x) for x in head.draft((t["H"].float() * 2).to(torch.bfloat16), 32)]
     assert np.array_equal(a[0], b[0])
     assert np.array_equal(2 * a[1], b[1]) and np.array_equal(2 * a[2], b[2])
+
+
+@pytest.mark.parametrize("B", [1, 8, 20])
+def test_draft_logits_equal_rescoring_bitwise(B):
+    """The draft call's logits (speculative per-slice rescoring and the merge's
+    own, on the few-row paths) are the bits fullhead_logits gives for the same
+    ids: every kernel uses one row-dot order."""
+    inp = gen.make_custom(20000, 5120, 128, B, "bf16", seed=31)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=32)
+    idx, score, lg = head.draft(t["H"], 32)
+    lg2 = head.logits(t["H"], idx)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(lg), np_(lg2))
+    errs, _ = check_lowrank(inp, 32, np_(idx), np_(score), np_(lg))
+    assert not errs, errs[:5]
+
+
+def test_one_row_pass_ties_inside_a_slice():
+    """One-row pass: nine bitwise copies of the best low-rank row at
+    consecutive ids. Every slice of that pass holds at least 64 rows, so nine
+    consecutive ids span at most two slices and five or more copies share
+    one; that slice's 4-entry list is full at the merge's bound, so the merge
+    also reads its raw scores. All copies come out first, in id order."""
+    V, k = 20000, 16
+    inp = gen.make_custom(V, 256, 64, 1, "bf16", seed=21)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=1, k_max=k)
+    tok = int(np_(head.candidates(t["H"], 1)[0])[0, 0])
+    start = 5000 if not 5000 <= tok < 5009 else 9000
+    dups = list(range(start, start + 9))
+    inp2 = dict(inp)
+    inp2["P"] = inp["P"].copy()
+    for dst in dups:
+        inp2["P"][dst] = inp["P"][tok]
+    P2 = dev(inp2["P"], DEV)
+    h2 = lr.Head(t["Q"], P2, t["W"], B_max=1, k_max=k)
+    idx, score, lg = h2.draft(t["H"], k)
+    torch.cuda.synchronize()
+    tied = sorted(dups + [tok])
+    assert np_(idx)[0, :10].tolist() == tied
+    assert len(set(np_(score)[0, :10].tolist())) == 1
+    errs, _ = check_lowrank(inp2, k, np_(idx), np_(score), np_(lg))
+    assert not errs, errs[:5]
 
 
 def test_duplicate_rows_tie_to_the_lower_id():
@@ -328,24 +375,42 @@ def test_ties_inside_one_slice_go_to_the_lower_ids(B):
     assert not errs, errs[:5]
 
 
-@pytest.mark.parametrize("V,d,r,B", [
-    (20000, 512, 128, 40),   # staged GEMM passes, split down-projection
-    (20000, 512, 128, 300),  # strip kernel (two batch tiles), split down-projection in the score scratch
+@pytest.mark.parametrize("V,d,r,B,dt,ties", [
+    (20000, 512, 128, 1, "bf16", False),   # one-row pass
+    (20000, 512, 128, 1, "bf16", True),    # one-row pass, boundary ties: the merge reads raw scores
+    (20000, 512, 128, 8, "bf16", False),   # eight-row streaming path
+    (20000, 512, 128, 8, "bf16", True),    # eight rows, boundary ties
+    (4096, 256, 32, 1, "fp32", False),     # fp32 (matrix-core slice lists and merge)
+    (20000, 512, 128, 40, "bf16", False),  # staged GEMM passes, split down-projection
+    (20000, 512, 128, 300, "bf16", False), # strip kernel (two batch tiles), split down-projection in the score scratch
 ])
-def test_repeat_calls_and_poisoned_workspace_are_bitwise_stable(V, d, r, B):
-    inp = gen.make_custom(V, d, r, B, "bf16", seed=6)
+def test_repeat_calls_and_poisoned_workspace_are_bitwise_stable(V, d, r, B, dt, ties):
+    """Repeated calls agree bit for bit, also after the workspace is filled
+    with garbage between calls: no call reads what an earlier call left. With
+    `ties`, all but 20 rows of P are zero, so that the k-th best score is a
+    tie shared by thousands of rows and the merges take their raw-score
+    paths."""
+    inp = gen.make_custom(V, d, r, B, dt, seed=6)
     t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    if ties:
+        t["P"][20:].zero_()
     head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=64)
-    say(f"[run] poisoned workspace V={V} d={d} r={r} B={B}")
+    say(f"[run] poisoned workspace V={V} d={d} r={r} B={B} {dt} ties={ties}")
     ref = [np_(x) for x in head.draft(t["H"], 64)]
     for trial in range(5):
         head.workspace.fill_(0xFF if trial % 2 else 0x7F)     # NaN / large garbage
         got = [np_(x) for x in head.draft(t["H"], 64)]
         for a, b in zip(ref, got):
-            assert np.array_equal(a, b)
+            assert np.array_equal(a, b, equal_nan=True)
     f1 = [np_(x) for x in head.full_topk(t["H"], 64)]
     f2 = [np_(x) for x in head.full_topk(t["H"], 64)]
     assert all(np.array_equal(a, b) for a, b in zip(f1, f2))
+    if ties:
+        inp2 = dict(inp)
+        inp2["P"] = inp["P"].copy()
+        inp2["P"][20:] = 0
+        errs, _ = check_lowrank(inp2, 64, *ref)
+        assert not errs, errs[:5]
 
 
 # ------------------------------------------- draft distribution (D1-D3)
