@@ -149,6 +149,28 @@ int lrhead_draft(lrhead_t h, const void* H, int64_t B, int k,
                  int32_t* idx, float* score, float* logits, void* stream);
 
 /*
+ * lrhead_draft without a handle and without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). The workspace is a
+ * device array inside the library, LRHEAD_STATIC_SCRATCH_MB MiB, one per GPU,
+ * held until the process ends; the first call on a device looks its address
+ * up (no allocation follows). Arguments as lrhead_create followed by
+ * lrhead_draft with B_max = B and k_max = k (Q, P, W, H device pointers in
+ * `dtype`; idx, score (may be NULL), logits: B x k). Returns
+ * LRHEAD_EWORKSPACE, before anything is enqueued, when the call needs more
+ * scratch than the array holds (lrhead_workspace_bytes(dtype, V, d, r, B, k)
+ * above LRHEAD_STATIC_SCRATCH_MB MiB; e.g. at V = 151936 the few-row path up
+ * to B = 8 fits). Calls on one GPU share the array, so calls that overlap in
+ * time on one GPU (different streams, or host threads) race and give wrong
+ * results; order them on one stream. Nothing in the array needs clearing:
+ * every call writes what it later reads.
+ */
+#define LRHEAD_STATIC_SCRATCH_MB 64
+int lrhead_draft_static(int dtype, int64_t V, int64_t d, int64_t r, const void* Q, const void* P,
+                        const void* W, const void* H, int64_t B, int k, int32_t* idx, float* score,
+                        float* logits, void* stream);
+
+/*
  * The draft distribution over each node's candidates and the node's branches
  * ("EAGLE-4: One Flexible Drafter for All Batch Sizes and Hardware":
  * section "Retrieve vocabulary candidates cheaply, then score them exactly",

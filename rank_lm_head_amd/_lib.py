@@ -15,6 +15,7 @@ FP32 = 1
 
 OK, EINVAL, ERANGE, EDTYPE, EALIGN, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6, -7
 K_MAX, R_MAX, D_MAX = 64, 512, 65536
+STATIC_SCRATCH_BYTES = 64 << 20   # LRHEAD_STATIC_SCRATCH_MB
 
 _c_i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -28,6 +29,8 @@ SIGNATURES = {
     "fullhead_logits": (ctypes.c_int, [_vp, _vp, _c_i64, _vp, ctypes.c_int, _vp, _vp]),
     "fullhead_topk": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp, _vp, _vp]),
     "lrhead_draft": (ctypes.c_int, [_vp, _vp, _c_i64, ctypes.c_int, _vp, _vp, _vp, _vp]),
+    "lrhead_draft_static": (ctypes.c_int, [ctypes.c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _c_i64,
+                                           ctypes.c_int, _vp, _vp, _vp, _vp]),
     "lrhead_branch": (ctypes.c_int, [_vp, _vp, _vp, _c_i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]),
     "lrhead_factor_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, ctypes.c_int]),
     "lrhead_factor": (ctypes.c_int, [_vp, _c_i64, _c_i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "launch.h"
@@ -38,6 +39,8 @@ struct lrhead_s {
   hipEvent_t ev_before;  // optional events attached to the score pass: its start
   hipEvent_t ev_after;   // and its end
 };
+
+static __device__ __align__(256) unsigned char scratch[size_t(LRHEAD_STATIC_SCRATCH_MB) << 20];
 
 namespace {
 
@@ -226,41 +229,24 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   return LRHEAD_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t lrhead_workspace_bytes(int dtype, int64_t V, int64_t d, int64_t r, int64_t B_max, int k_max) {
-  if (check_shapes(dtype, V, d, r, B_max, k_max) != LRHEAD_OK) return 0;
-  return layout(dtype, V, r, B_max, k_max).total;
-}
-
-int lrhead_create(lrhead_t* out, int dtype, int64_t V, int64_t d, int64_t r, const void* Q, const void* P,
-                  const void* W, int64_t B_max, int k_max, void* workspace, size_t workspace_bytes) {
-  if (!out) return fail(LRHEAD_EINVAL, "out is NULL");
-  *out = nullptr;
-  LRH_TRY(check_shapes(dtype, V, d, r, B_max, k_max));
-  if (!Q || !P || !W) return fail(LRHEAD_EINVAL, "Q, P and W must be non-NULL");
-  if (!workspace) return fail(LRHEAD_EINVAL, "workspace is NULL");
-  if (!aligned16(Q) || !aligned16(P) || !aligned16(W) || !aligned16(workspace))
-    return fail(LRHEAD_EALIGN, "Q, P, W and workspace must be 16-byte aligned");
-  const Layout L = layout(dtype, V, r, B_max, k_max);
-  if (workspace_bytes < L.total)
-    return fail(LRHEAD_EWORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, L.total);
-
+// The checks and settings a handle needs from the current device: it must be
+// gfx950; the GEMM kernels of row batches get their LDS limit raised; the
+// one-row pass sizes its grid by the compute units.
+int device_setup(int dtype, int64_t B_max, int* n_cu) {
   int dev = 0;
   LRH_HIP(hipGetDevice(&dev), "hipGetDevice");
   hipDeviceProp_t prop;
   LRH_HIP(hipGetDeviceProperties(&prop, dev), "hipGetDeviceProperties");
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(LRHEAD_EDEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
-
   if (lrh::batch_path(dtype, B_max)) LRH_HIP(lrh::batch_init(), "GEMM kernel set-up");
-  int n_cu = 0;
-  LRH_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev), "hipDeviceGetAttribute");
+  LRH_HIP(hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev), "hipDeviceGetAttribute");
+  return LRHEAD_OK;
+}
 
-  lrhead_s* h = new (std::nothrow) lrhead_s;
-  if (!h) return fail(LRHEAD_EINVAL, "out of host memory");
+void fill_handle(lrhead_s* h, int dtype, int64_t V, int64_t d, int64_t r, const void* Q, const void* P,
+                 const void* W, int64_t B_max, int k_max, void* workspace, size_t workspace_bytes, int n_cu) {
+  const Layout L = layout(dtype, V, r, B_max, k_max);
   h->magic = kMagic;
   h->dtype = dtype;
   h->V = V;
@@ -285,6 +271,71 @@ int lrhead_create(lrhead_t* out, int dtype, int64_t V, int64_t d, int64_t r, con
   h->bw = h->batch ? lrh::batch_scratch(h->ws + L.batch, V, B_max) : lrh::BatchScratch{};
   h->ev_before = nullptr;
   h->ev_after = nullptr;
+}
+
+// ------------------------------------------------- allocation-free variant
+// The workspace of lrhead_draft_static is `scratch` (file scope, below the
+// namespace): one copy per GPU, resident until the process ends. In host
+// code its name only stands for the symbol; its address on a device comes
+// from hipGetSymbolAddress with that device current, looked up once per
+// device and kept.
+constexpr size_t kStaticScratchBytes = size_t(LRHEAD_STATIC_SCRATCH_MB) << 20;
+constexpr int kMaxDevices = 64;
+struct StaticDevice {
+  bool ready;
+  void* ptr;   // device address of `scratch` on this device
+  int n_cu;
+};
+std::mutex g_static_mu;
+StaticDevice g_static[kMaxDevices];
+
+int static_device(int dtype, int64_t B, void** ptr, int* n_cu) {
+  int dev = 0;
+  LRH_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LRHEAD_EDEVICE, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDevice& sd = g_static[dev];
+  if (!sd.ready) {
+    int cu = 0;
+    LRH_TRY(device_setup(dtype, 1, &cu));
+    void* p = nullptr;
+    LRH_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    sd.ptr = p;
+    sd.n_cu = cu;
+    sd.ready = true;
+  }
+  if (lrh::batch_path(dtype, B)) LRH_HIP(lrh::batch_init(), "GEMM kernel set-up");
+  *ptr = sd.ptr;
+  *n_cu = sd.n_cu;
+  return LRHEAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lrhead_workspace_bytes(int dtype, int64_t V, int64_t d, int64_t r, int64_t B_max, int k_max) {
+  if (check_shapes(dtype, V, d, r, B_max, k_max) != LRHEAD_OK) return 0;
+  return layout(dtype, V, r, B_max, k_max).total;
+}
+
+int lrhead_create(lrhead_t* out, int dtype, int64_t V, int64_t d, int64_t r, const void* Q, const void* P,
+                  const void* W, int64_t B_max, int k_max, void* workspace, size_t workspace_bytes) {
+  if (!out) return fail(LRHEAD_EINVAL, "out is NULL");
+  *out = nullptr;
+  LRH_TRY(check_shapes(dtype, V, d, r, B_max, k_max));
+  if (!Q || !P || !W) return fail(LRHEAD_EINVAL, "Q, P and W must be non-NULL");
+  if (!workspace) return fail(LRHEAD_EINVAL, "workspace is NULL");
+  if (!aligned16(Q) || !aligned16(P) || !aligned16(W) || !aligned16(workspace))
+    return fail(LRHEAD_EALIGN, "Q, P, W and workspace must be 16-byte aligned");
+  const Layout L = layout(dtype, V, r, B_max, k_max);
+  if (workspace_bytes < L.total)
+    return fail(LRHEAD_EWORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, L.total);
+  int n_cu = 0;
+  LRH_TRY(device_setup(dtype, B_max, &n_cu));
+  lrhead_s* h = new (std::nothrow) lrhead_s;
+  if (!h) return fail(LRHEAD_EINVAL, "out of host memory");
+  fill_handle(h, dtype, V, d, r, Q, P, W, B_max, k_max, workspace, workspace_bytes, n_cu);
   *out = h;
   return LRHEAD_OK;
 }
@@ -356,6 +407,30 @@ int lrhead_draft(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, floa
   LRH_TRY(check_out(logits, "logits", B > 0));
   if (B == 0) return LRHEAD_OK;
   return enqueue_head(h, H, B, k, idx, score, logits, static_cast<hipStream_t>(stream));
+}
+
+int lrhead_draft_static(int dtype, int64_t V, int64_t d, int64_t r, const void* Q, const void* P, const void* W,
+                        const void* H, int64_t B, int k, int32_t* idx, float* score, float* logits, void* stream) {
+  if (B < 0) return fail(LRHEAD_ERANGE, "B = %lld is negative", (long long)B);
+  LRH_TRY(check_shapes(dtype, V, d, r, B > 0 ? B : 1, k));
+  if (!Q || !P || !W) return fail(LRHEAD_EINVAL, "Q, P and W must be non-NULL");
+  if (!aligned16(Q) || !aligned16(P) || !aligned16(W)) return fail(LRHEAD_EALIGN, "Q, P and W must be 16-byte aligned");
+  if (B > 0 && !H) return fail(LRHEAD_EINVAL, "H is NULL");
+  if (!aligned16(H)) return fail(LRHEAD_EALIGN, "H is not 16-byte aligned");
+  LRH_TRY(check_out(idx, "idx", B > 0));
+  LRH_TRY(check_out(score, "score", false));
+  LRH_TRY(check_out(logits, "logits", B > 0));
+  if (B == 0) return LRHEAD_OK;
+  const size_t need = layout(dtype, V, r, B, k).total;
+  if (need > kStaticScratchBytes)
+    return fail(LRHEAD_EWORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu", need,
+                kStaticScratchBytes);
+  void* ws = nullptr;
+  int n_cu = 0;
+  LRH_TRY(static_device(dtype, B, &ws, &n_cu));
+  lrhead_s h;
+  fill_handle(&h, dtype, V, d, r, Q, P, W, B, k, ws, kStaticScratchBytes, n_cu);
+  return enqueue_head(&h, H, B, k, idx, score, logits, static_cast<hipStream_t>(stream));
 }
 
 int lrhead_branch(const float* logits, const int32_t* idx, const float* parent, int64_t B, int k, int nb,

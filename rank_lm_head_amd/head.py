@@ -149,6 +149,34 @@ class Head:
             pass
 
 
+def draft_static(Q: torch.Tensor, P: torch.Tensor, W: torch.Tensor, H: torch.Tensor, k: int, *,
+                 want_score: bool = True, out=None):
+    """One draft-head call through lrhead_draft_static: no handle and no
+    workspace (the library's own device scratch); returns (idx, score or
+    None, logits), all [B, k]. Outputs are allocated here unless `out`
+    gives them."""
+    _need(Q.dtype in _DTYPES and P.dtype == Q.dtype and W.dtype == Q.dtype and H.dtype == Q.dtype,
+          "Q, P, W and H must share a supported dtype")
+    for name, t in (("Q", Q), ("P", P), ("W", W), ("H", H)):
+        _need(t.is_cuda and t.device == Q.device and t.is_contiguous() and t.dim() == 2,
+              f"{name} must be a contiguous matrix on {Q.device}")
+    r, d = Q.shape
+    V = P.shape[0]
+    B = H.shape[0]
+    _need(tuple(P.shape) == (V, r) and tuple(W.shape) == (V, d) and H.shape[1] == d, "shapes of Q, P, W, H disagree")
+    if out is None:
+        idx = torch.empty((B, k), dtype=torch.int32, device=Q.device)
+        score = torch.empty((B, k), dtype=torch.float32, device=Q.device) if want_score else None
+        logits = torch.empty((B, k), dtype=torch.float32, device=Q.device)
+    else:
+        idx, score, logits = out
+    lib = _lib.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(Q.device).cuda_stream)
+    _lib.check(lib.lrhead_draft_static(_DTYPES[Q.dtype], V, d, r, _ptr(Q), _ptr(P), _ptr(W), _ptr(H), B, k,
+                                       _ptr(idx), _ptr(score), _ptr(logits), stream), "lrhead_draft_static")
+    return idx, score, logits
+
+
 def branch(logits: torch.Tensor, idx: torch.Tensor, nb: int, parent: torch.Tensor | None = None):
     """Draft distribution over each row's candidates and its nb branches.
 
