@@ -60,6 +60,12 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// A 16-byte load of data read once (a streamed weight matrix): non-temporal,
+// so that it does not push code and reused data out of the caches.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // ---------------------------------------------------------------- MFMA tile
 // acc += A_rows . B_rows^T over [0, K) for one 16x16 tile. `a` and `b` point
 // at the lane's own row (row l & 15 of each operand); a_ok / b_ok say whether

@@ -14,6 +14,7 @@ namespace lrh {
 
 // Scores of rows [wlo, whi) of M (V x K, bf16) against the NB rows of X
 // (B x K, bf16; rows past B score nothing) into sc[b * ldsc + (v - blo)].
+// M is read once per call, with non-temporal loads.
 // The z loads go first and are widened only after the first group of M
 // loads is issued. Rows past the wave's range are loaded from its last row
 // (a valid address, so no load is predicated) and never kept; a wave
@@ -45,7 +46,7 @@ __device__ __forceinline__ void stream_scores(const uint16_t* __restrict__ M, co
 #pragma unroll
     for (int t = 0; t < U; ++t) {
       const int64_t row = base + t * RPL + sub;
-      buf[t] = load16(M + (row < last ? row : last) * K + 8 * c);
+      buf[t] = load16_stream(M + (row < last ? row : last) * K + 8 * c);
     }
   };
   auto consume = [&](const u32x4 (&buf)[U], int64_t base) {
