@@ -277,13 +277,30 @@ def latency_table(torch, lr, dev, steps: int) -> dict:
 
 
 def recall_sweep(torch, lr, dev, rows: int = 256) -> dict:
-    """Recall of the full head's top-b inside the low-rank top-k: for each r,
-    the share of each row's b best full-head tokens (exact logits over all V)
-    that the low-rank candidates of that row contain, averaged over rows."""
+    """Recall of the full head's top-b inside the low-rank top-k, on the heads
+    of gen/ (the workload recipe: r = 128 and r = 512 are the batch-1
+    configurations, r = 256 the same recipe, each with `rows` i.i.d. rows):
+    the share of each row's b best full-head tokens (fullhead_topk, exact
+    logits over all V) among its k low-rank candidates (lrhead_candidates),
+    averaged over rows. The GPU tests check this table against the oracle's
+    own lists, at small heads and at these shapes."""
+    import numpy as np
+    import gen
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
     out = []
-    H = synthetic_rows(torch, dev, rows, TABLE_D, 4242)
     for r in TABLE_R:
-        Q, P, W = synthetic_head(torch, dev, TABLE_V, TABLE_D, r, seed=7000 + r)
+        if r == 128:
+            inp = gen.make(2, B=rows)
+        elif r == 512:
+            inp = gen.make(3, B=rows)
+        else:
+            inp = gen.make_custom(TABLE_V, TABLE_D, r, rows, "bf16", seed=r)
+        Q, P, W, H = (to_dev(inp[x]) for x in ("Q", "P", "W", "H"))
         head = lr.Head(Q, P, W, B_max=rows, k_max=64)
         cidx, _ = head.candidates(H, 64)
         fidx, _ = head.full_topk(H, 8)
@@ -291,13 +308,14 @@ def recall_sweep(torch, lr, dev, rows: int = 256) -> dict:
         f = fidx.cpu().numpy()
         for b in (1, 4, 8):
             for k in (8, 16, 32, 64):
-                hit = [len(set(f[i, :b].tolist()) & set(c[i, :k].tolist())) / b for i in range(rows)]
-                out.append({"r": r, "b": b, "k": k, "recall": round(float(sum(hit) / rows), 4)})
+                hit = sum(len(set(f[i, :b].tolist()) & set(c[i, :k].tolist())) for i in range(rows))
+                out.append({"r": r, "b": b, "k": k, "recall": round(hit / (b * rows), 4)})
         head.close()
-        del head, Q, P, W
+        del head, Q, P, W, H, inp
         torch.cuda.empty_cache()
     return {"recall": "share of the full head's top-b found in the low-rank top-k", "V": TABLE_V,
-            "d": TABLE_D, "rows": rows, "noise": "W = P.Q + 0.1 E", "data": "synthetic", "results": out}
+            "d": TABLE_D, "rows": rows, "heads": "gen/: W = round(P.Q + 0.1 E), i.i.d. RMS-normalised rows",
+            "data": "synthetic", "results": out}
 
 
 def factor_timing(torch, lr, dev, reps: int = 3) -> dict:

@@ -14,3 +14,4 @@ from .compare import (  # noqa: F401
     check_candidates, check_logits, check_scores, band_counts, ulp_bf16,
     z_step_allowance, LOGIT_RTOL, SCORE_TOL,
 )
+from . import recall  # noqa: F401,E402

@@ -7,11 +7,12 @@ library; both take their inputs from the ``gen`` module.
 
 What it computes follows "EAGLE-4" (yuxiaoba.github.io/tech/en/eagle-4),
 section "Retrieve vocabulary candidates cheaply, then score them exactly":
-a low-rank head over the *full* vocabulary retrieves candidate tokens, and
-only those candidates are then given their exact logits by the original
-full-rank head. The alphasignal news page (section "Runtime-sized
-speculation", item "Low-rank candidate head") adds that token prediction is
-factored into smaller matrices. Written out, for each draft row b:
+every token of the vocabulary is first ranked with a cheap rank-r
+factorisation of the head, the k best ranked tokens are kept, and the
+original head's weights then give those k tokens, and no others, their exact
+logits. The alphasignal news page (section "Runtime-sized speculation", item
+"Low-rank candidate head") describes the same head as a factorisation of the
+token prediction into two smaller matrices. Written out, for each draft row b:
 
   O1  z_b  = Q . h_b                      (rank r), stored in the weight dtype
   O2  s_b[v] = P[v, :] . z_b              for every vocabulary row v

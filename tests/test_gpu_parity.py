@@ -538,3 +538,59 @@ def test_factor_at_the_drafter_head_size():
     err = torch.linalg.norm(Wf[rows] - Pf[rows] @ Qf)
     planted = torch.linalg.norm(Wf[rows] - t["P"][rows].float() @ t["Q"].float())
     assert err <= 1.02 * planted, (float(err), float(planted))
+
+
+# ------------------------------------------------ retrieval recall (f2)
+
+RECALL_B, RECALL_K = (1, 4, 8), (8, 16, 32, 64)
+
+
+def _recall_against_the_oracle(inp, t, rows):
+    """recall(b, k) from the two GPU paths (lrhead_candidates, fullhead_topk)
+    and from the oracle's own lists, row by row: equal on every row whose GPU
+    lists are the oracle's; elsewhere the lists must differ from the
+    oracle's by tie-band swaps only (the parity rule)."""
+    from oracle import recall
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=t["H"].shape[0], k_max=64)
+    cidx, _ = head.candidates(t["H"], max(RECALL_K))
+    fidx, flog = head.full_topk(t["H"], max(RECALL_B))
+    torch.cuda.synchronize()
+    c, f, fl = np_(cidx).astype(np.int64), np_(fidx).astype(np.int64), np_(flog)
+    head.close()
+    errs, _ = check_lowrank(inp, max(RECALL_K), c, None, None, rows=rows)
+    assert not errs, errs[:4]
+    errs, _ = check_full(inp, max(RECALL_B), f, fl, rows=rows)
+    assert not errs, errs[:4]
+    ref = recall.recall_sweep(inp["Q"], inp["P"], inp["W"], inp["H"], inp["cfg"].dtype, RECALL_B, RECALL_K,
+                              rows=rows)
+    got = recall.recall_table(c[rows], f[rows], RECALL_B, RECALL_K)
+    n_diff = 0
+    for eg, eo in zip(got, ref["table"]):
+        b, k = eg["b"], eg["k"]
+        for i in range(len(rows)):
+            same = (set(c[rows[i], :k].tolist()) == set(ref["cand_idx"][i, :k].tolist())
+                    and set(f[rows[i], :b].tolist()) == set(ref["full_idx"][i, :b].tolist()))
+            if same:
+                assert eg["hits"][i] == eo["hits"][i], (b, k, rows[i])
+            else:
+                n_diff += int(eg["hits"][i] != eo["hits"][i])
+    say(f"[recall] " + " ".join(f"b{e['b']}k{e['k']}={e['recall']:.3f}" for e in got)
+        + f" (rows differing by tie-band swaps: {n_diff})")
+    return got
+
+
+@pytest.mark.parametrize("r", [16, 32, 64])
+def test_recall_from_the_gpu_paths_matches_the_oracle(r):
+    inp = gen.make_custom(6000, 512, r, 24, "bf16", seed=r)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    got = _recall_against_the_oracle(inp, t, np.arange(24))
+    for e in got:   # at k = 64 of 6000 tokens the best full-head token is retrieved in most rows
+        if e["b"] == 1 and e["k"] == 64:
+            assert e["recall"] >= 0.5
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("cid", [2, 3])
+def test_recall_at_the_drafter_head_size(cid):
+    inp, t = config(cid)
+    _recall_against_the_oracle(inp, t, np.arange(inp["H"].shape[0]))

@@ -510,3 +510,64 @@ def test_factor_orth_is_cholesky_qr2():
     assert np.allclose(Y.T @ Y, np.eye(9), atol=1e-13)
     Qh, _ = np.linalg.qr(X)
     assert np.allclose(np.abs(Y.T @ Qh), np.eye(9), atol=1e-10)    # same columns up to sign
+
+
+# ------------------------------------------------ retrieval recall (f2)
+
+def test_recall_hand_intersections():
+    from oracle import recall
+    cand = np.array([[3, 1, 2, 7], [0, 5, 6, 9]])
+    full = np.array([[1, 5, 4], [6, 0, 2]])
+    # row 0: {1, 5} & {3, 1, 2} = {1}; row 1: {6, 0} & {0, 5, 6} = {0, 6}
+    assert recall.recall_hits(cand, full, 2, 3).tolist() == [1, 2]
+    # row 0: {1, 5, 4} & {3, 1, 2, 7} = {1}; row 1: {6, 0, 2} & {0, 5, 6, 9} = {0, 6}
+    assert recall.recall_hits(cand, full, 3, 4).tolist() == [1, 2]
+    t = recall.recall_table(cand, full, [1], [1, 4])
+    assert [(e["b"], e["k"], e["recall"]) for e in t] == [(1, 1, 0.0), (1, 4, 1.0)]
+    with pytest.raises(ValueError):
+        recall.recall_hits(cand, full, 4, 2)
+
+
+def test_recall_of_an_exactly_factorised_head_is_min_k_b_over_b():
+    # small integers: W = P.Q, z = Q.h and both stages are exact in fp32, so
+    # the low-rank scores are the full logits and the two orders coincide
+    from oracle import recall
+    rng = np.random.default_rng(5)
+    V, d, r, n = 40, 6, 6, 5
+    Q = rng.integers(-3, 4, (r, d)).astype(np.float32)
+    P = rng.integers(-3, 4, (V, r)).astype(np.float32)
+    W = (P.astype(np.float64) @ Q.astype(np.float64)).astype(np.float32)
+    H = rng.integers(-3, 4, (n, d)).astype(np.float32)
+    sw = recall.recall_sweep(Q, P, W, H, "fp32", bs=[1, 3, 5], ks=[1, 2, 3, 5, 8, 40])
+    for e in sw["table"]:
+        assert e["recall"] == min(e["k"], e["b"]) / e["b"], e
+
+
+def test_recall_of_a_negated_head_has_its_closed_form():
+    # P = -W with Q = I: the low-rank order is the full order reversed, so
+    # F_b and C_k overlap in max(0, k - (V - b)) tokens (no ties: continuous W)
+    from oracle import recall
+    rng = np.random.default_rng(11)
+    V, d, n = 12, 5, 4
+    W = rng.standard_normal((V, d)).astype(np.float32)
+    P = -W
+    Q = np.eye(d, dtype=np.float32)
+    H = rng.standard_normal((n, d)).astype(np.float32)
+    sw = recall.recall_sweep(Q, P, W, H, "fp32", bs=[1, 3, 5], ks=list(range(1, V + 1)))
+    for e in sw["table"]:
+        assert e["recall"] == max(0, e["k"] - (V - e["b"])) / e["b"], e
+
+
+def test_recall_is_one_at_k_equals_v_and_grows_with_k():
+    from oracle import recall
+    inp = gen.make_custom(300, 64, 8, 6, "bf16", seed=3)
+    ks = [1, 2, 4, 8, 16, 32, 64, 128, 300]
+    sw = recall.recall_sweep(inp["Q"], inp["P"], inp["W"], inp["H"], "bf16", bs=[1, 4, 8], ks=ks)
+    by_b = {}
+    for e in sw["table"]:
+        by_b.setdefault(e["b"], []).append(e["recall"])
+    for b, rs in by_b.items():
+        assert rs[-1] == 1.0
+        assert all(x <= y for x, y in zip(rs, rs[1:])), (b, rs)
+    # the oracle's lists are its own O3 / O5 orders
+    assert np.array_equal(sw["cand_idx"], oracle.lowrank_head(inp["Q"], inp["P"], None, inp["H"], 300, "bf16")["idx"])
