@@ -84,8 +84,12 @@ struct StageDma {
   int col[LD];        // first column of the lane's chunk in stage 0
   uint32_t oob;       // an offset past the resource
 
-  __device__ __forceinline__ void init(const uint16_t* __restrict__ base, int64_t row0, int64_t nrows, int K) {
-    const int64_t valid = nrows - row0;   // >= 1
+  // The resource covers the block's own tile_rows rows from row0 (fewer at
+  // the matrix's end): at most 256 rows of at most 65536 columns, 32 MiB,
+  // so its 32-bit size cannot wrap however large the matrix is.
+  __device__ __forceinline__ void init(const uint16_t* __restrict__ base, int64_t row0, int64_t nrows, int K,
+                                       int tile_rows) {
+    const int64_t valid = min(nrows - row0, (int64_t)tile_rows);   // >= 1
     const uint32_t bytes = uniform_u32((uint32_t)(valid * K * 2));
     const uint64_t addr = reinterpret_cast<uint64_t>(base + row0 * (int64_t)K);
     const uint64_t ua = ((uint64_t)uniform_u32((uint32_t)(addr >> 32)) << 32) | uniform_u32((uint32_t)addr);
@@ -184,8 +188,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
   const bool ktail = (K % kBK) != 0;
   StageDma<C::A_LD> la;
   StageDma<C::B_LD> lb;
-  la.init(M, m0, V, K);
-  lb.init(X, n0, B, K);
+  la.init(M, m0, V, K, C::BM);
+  lb.init(X, n0, B, K, C::BN);
   // Stage kc lives in buffer kc % nbuf; ST - 1 stages are in flight while
   // one is used.
   static_assert(C::ST == 2 || C::ST == 3, "two or three stage buffers");

@@ -594,3 +594,37 @@ def test_recall_from_the_gpu_paths_matches_the_oracle(r):
 def test_recall_at_the_drafter_head_size(cid):
     inp, t = config(cid)
     _recall_against_the_oracle(inp, t, np.arange(inp["H"].shape[0]))
+
+
+# ------------------------------------------------ 4 GiB of full-head weights
+
+@pytest.mark.timeout(900)
+def test_full_head_with_4_gib_of_weights():
+    # V * d * 2 bytes = 2^32: the batch path's tile copies size their buffer
+    # to the block's tile, not to the rest of the matrix, so no size wraps.
+    # Rows 0 .. 4 (the first tile) are planted as the rows' clear winners.
+    V, d, B, k, r = 262144, 8192, 5, 8, 8
+    g = torch.Generator(device=DEV).manual_seed(77)
+    sd = 1.0 / math.sqrt(d)
+    W = torch.empty(V, d, dtype=torch.bfloat16, device=DEV)
+    for c0 in range(0, V, 16384):
+        W[c0:c0 + 16384] = (torch.randn(16384, d, generator=g, device=DEV) * sd).to(torch.bfloat16)
+    h = torch.randn(B, d, generator=g, device=DEV)
+    H = (h / h.pow(2).mean(dim=1, keepdim=True).sqrt()).to(torch.bfloat16)
+    W[:B] = (4.0 * H.float() * sd).to(torch.bfloat16)
+    Q = (torch.randn(r, d, generator=g, device=DEV) * sd).to(torch.bfloat16)
+    P = (torch.randn(V, r, generator=g, device=DEV) * sd).to(torch.bfloat16)
+    head = lr.Head(Q, P, W, B_max=B, k_max=k)
+    say("[run] full_topk, V=262144 d=8192 B=5")
+    fidx, flog = head.full_topk(H, k)
+    torch.cuda.synchronize()
+    head.close()
+    idx, lg = np_(fidx).astype(np.int64), np_(flog)
+    assert idx[:, 0].tolist() == list(range(B))
+    inp = {"cfg": gen.HeadConfig(0, "4 GiB W", B, d, V, r, k, "bf16", "iid"),
+           "W": W.view(torch.int16).cpu().numpy().view(np.uint16),
+           "H": H.view(torch.int16).cpu().numpy().view(np.uint16)}
+    del W, P
+    torch.cuda.empty_cache()
+    errs, _ = check_full(inp, k, idx, lg)
+    assert not errs, errs[:4]
