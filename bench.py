@@ -44,10 +44,13 @@ _CSRC = "rank_lm_head_amd/csrc/"
 # The sources each measured kernel is built from: its committed HBM counters
 # stay valid while these are unchanged.
 KERNEL_SOURCES = {
-    name: [_CSRC + f for f in (src, "topk.h", "device.h", "launch.h")]
-    for name, src in (("select_short_kernel", "kernels_small.hip"), ("select_mfma_kernel", "kernels_mfma.hip"),
-                      ("gemm_sel_kernel", "kernels_gemm.hip"), ("strip_sel_kernel", "kernels_gemm.hip"))
+    name: [_CSRC + f for f in srcs + ("topk.h", "device.h", "launch.h")]
+    for name, srcs in (("select_short_kernel", ("kernels_small.hip", "stream.h")),
+                       ("select_mfma_kernel", ("kernels_mfma.hip",)),
+                       ("gemm_sel_kernel", ("kernels_gemm.hip",)), ("strip_sel_kernel", ("kernels_gemm.hip",)),
+                       ("draft1_kernel", ("kernels_b1.hip", "merge.h", "stream.h")))
 }
+B1_MAX_BLOCKS, B1_MAX_ROWS_PER_BLOCK, N_CU = 512, 16 * 64, 256
 
 
 def parse():
@@ -69,6 +72,18 @@ def parse():
     ap.add_argument("--factor", action="store_true",
                     help="instead of the headline: time building P and Q from W (r = 128/256/512, one "
                          "subspace iteration) at V=151936, d=5120, one JSON object")
+    ap.add_argument("--peak", action="store_true",
+                    help="instead of the headline: the achievable-peak probes (HBM read bandwidth of a "
+                         "plain streaming read at P's size and at 1 GiB, bf16 GEMM rate of the vendor "
+                         "library), one JSON object")
+    ap.add_argument("--draft-only", action="store_true",
+                    help="time only the draft-head call (no full-head baseline, vendor GEMM or CPU "
+                         "oracle): the run to put under rocprofv3 for the counters of the draft path")
+    ap.add_argument("--summarise-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="instead of the headline: turn two rocprofv3 counter_collection.csv files "
+                         "(FETCH_SIZE, WRITE_SIZE) of a --draft-only run with --copy-calibration-mib "
+                         "into profiles/counters.json entries for --config (keyed by the full kernel "
+                         "name) and print a markdown table")
     ap.add_argument("--recall", action="store_true",
                     help="instead of the headline: recall of the full head's top-b inside the "
                          "low-rank top-k for r in 128/256/512, one JSON object")
@@ -108,18 +123,71 @@ def kernel_hash(kernel: str) -> str:
 
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes (read + written) per launch of `kernel` from the committed
-    rocprofv3 counter summary (FETCH_SIZE / WRITE_SIZE, scaled by a copy of
-    known size), if it was taken on the current kernel sources; else None."""
+    rocprofv3 counter summary (FETCH_SIZE / WRITE_SIZE of a --draft-only run,
+    scaled by a copy of known size; written by --summarise-counters), if it
+    was taken on the current kernel sources; else None. Entries are keyed by
+    the full kernel name: of the instantiations of `kernel` in that run, the
+    one that moves the most bytes per launch (the main pass where a kernel
+    also runs as a sampling pass)."""
     path = os.path.join(ROOT, "profiles", "counters.json")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
         return None
     try:
-        rec = json.load(open(path))[workload][kernel]
+        recs = json.load(open(path))[workload]
     except Exception:
         return None
-    if kernel not in KERNEL_SOURCES or rec.get("kernel_hash") != kernel_hash(kernel):
+    mine = [r for name, r in recs.items() if isinstance(r, dict) and f"lrh::{kernel}<" in name]
+    if not mine:
+        return None
+    rec = max(mine, key=lambda r: r["bytes_per_launch"])
+    if rec.get("kernel_hash") != kernel_hash(kernel):
         return None
     return float(rec["bytes_per_launch"])
+
+
+def summarise_counters(fetch_csv: str, write_csv: str, workload: str, calib_mib: int) -> str:
+    """counters.json entries for `workload` from a FETCH_SIZE and a WRITE_SIZE
+    rocprofv3 run (counter_collection.csv), scaled so that the calibration
+    copy of calib_mib MiB (__amd_rocclr_copyBuffer) reads and writes exactly
+    its size; returns a markdown table of the figures."""
+    import csv
+
+    def per_kernel(path):
+        acc = {}
+        for row in csv.DictReader(open(path)):
+            name = row["Kernel_Name"]
+            a = acc.setdefault(name, {"dispatches": set(), "kib": 0.0})
+            a["dispatches"].add(row.get("Dispatch_Id") or row.get("Correlation_Id"))
+            a["kib"] += float(row["Counter_Value"])
+        return {n: (len(a["dispatches"]), a["kib"]) for n, a in acc.items()}
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    cal = calib_mib * 1024.0
+    cf = [v for n, v in fetch.items() if "copyBuffer" in n]
+    cw = [v for n, v in write.items() if "copyBuffer" in n]
+    f_scale = cal / (cf[0][1] / cf[0][0]) if cf else 1.0
+    w_scale = cal / (cw[0][1] / cw[0][0]) if cw else 1.0
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    allrec = json.load(open(path)) if os.path.exists(path) else {}
+    recs = {}
+    lines = [f"Calibration: a {calib_mib} MiB device copy; FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}.",
+             "", "| Kernel | Dispatches | read MB / launch | written MB / launch |", "|---|---|---|---|"]
+    for name, (nd, kib) in fetch.items():
+        if "copyBuffer" in name:
+            continue
+        wk = write.get(name, (nd, 0.0))[1]
+        rd = kib / nd * 1024 * f_scale
+        wr = wk / nd * 1024 * w_scale
+        rec = {"dispatches": nd, "read_bytes": rd, "written_bytes": wr, "bytes_per_launch": rd + wr}
+        for base in KERNEL_SOURCES:
+            if f"lrh::{base}<" in name:
+                rec["kernel_hash"] = kernel_hash(base)
+        recs[name] = rec
+        lines.append(f"| `{name[:110]}` | {nd} | {rd / 1e6:.3f} | {wr / 1e6:.3f} |")
+    allrec[workload] = recs
+    with open(path, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+    return "\n".join(lines)
 
 
 def timed_graph_replays(torch, graph, n_replays: int) -> float:
@@ -168,37 +236,111 @@ def event_timed(torch, hip, heads, fn, n: int) -> float:
     return sum(ms) / len(ms) * 1e-3
 
 
-def cpu_baseline(inp: dict, seconds: float) -> dict:
-    """The float64 oracle (steps O1-O4 of the method) on the host cores."""
-    import platform
-
-    import oracle
+def host_model() -> str:
+    """The host CPU as lscpu names it (model, sockets x cores x threads)."""
+    import subprocess
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        f = dict(ln.split(":", 1) for ln in out.splitlines() if ":" in ln)
+        g = lambda k: f.get(k, "?").strip()
+        return (f"{g('Model name')}, {g('Socket(s)')} socket(s) x {g('Core(s) per socket')} cores x "
+                f"{g('Thread(s) per core')} threads, {g('CPU(s)')} logical CPUs")
     except Exception:
-        threads = 1
-    cfg = inp["cfg"]
-    model = platform.processor() or "unknown"
-    try:
         for ln in open("/proc/cpuinfo"):
             if ln.startswith("model name"):
-                model = ln.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.lowrank_head(inp["Q"], inp["P"], inp["W"], inp["H"], cfg.k, cfg.dtype)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+                return ln.split(":", 1)[1].strip()
+    return "unknown"
+
+
+def cpu_baseline(inp: dict, seconds: float) -> dict:
+    """The float64 oracle (steps O1-O4 of the method) on the host cores: with
+    all the BLAS threads NumPy uses, and with one thread."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threadpool_limits = None
+        threads = 1
+    cfg = inp["cfg"]
+    model = host_model()
+
+    def rate(limit_s):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.lowrank_head(inp["Q"], inp["P"], inp["W"], inp["H"], cfg.k, cfg.dtype)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= limit_s:
+                return n, el
+
+    n, el = rate(seconds)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            n1, el1 = rate(seconds / 2)
+        one = {"value": n1 * cfg.B / el1, "unit": "rows/s", "cores": 1,
+               "sample": f"{n1} calls in {el1:.1f} s, BLAS limited to one thread"}
     return {"value": n * cfg.B / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} full draft-head calls of the benchmark workload (B={cfg.B}) in {el:.1f} s "
-                      f"(float64 NumPy, BLAS threads {threads}, host {os.cpu_count()} logical CPUs, {model})",
-            "us_per_call": el / n * 1e6}
+                      f"(float64 NumPy, BLAS threads {threads}, host: {model})",
+            "one_thread": one, "host": model, "us_per_call": el / n * 1e6}
+
+
+# ------------------------------------------------ achievable peaks
+def probe_hbm_read(torch, dev, nbytes: int, rotate: int, reps: int) -> float:
+    """Achievable HBM read bandwidth (GB/s) of a plain streaming read
+    (csrc/probe_read.hip) over `rotate` distinct buffers of nbytes each, read
+    in turn (cache-cold when rotate * nbytes is well past the 256 MB
+    Infinity Cache), timed by HIP events around each launch."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(ROOT, "rank_lm_head_amd", "libprobe.so"))
+    lib.probe_read.argtypes = [C.c_void_p, C.c_size_t, C.c_uint32, C.c_void_p, C.c_int, C.c_void_p]
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(i + 1) for i in range(rotate)]
+    sink = torch.zeros(4, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    best = 0.0
+    for blocks in (N_CU * 2, N_CU * 4, N_CU * 8):
+        for i in range(rotate):   # warm-up
+            assert lib.probe_read(bufs[i].data_ptr(), nbytes, 0x9E3779B9, sink.data_ptr(), blocks, stream) == 0
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for j in range(reps):
+            evs[j][0].record()
+            lib.probe_read(bufs[j % rotate].data_ptr(), nbytes, 0x9E3779B9, sink.data_ptr(), blocks, stream)
+            evs[j][1].record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        best = max(best, nbytes / (ms[len(ms) // 2] * 1e-3) / 1e9)
+    del bufs
+    torch.cuda.empty_cache()
+    return best
+
+
+def probe_mfma_bf16(torch, dev, n: int = 8192, reps: int = 20) -> float:
+    """Achievable dense bf16 matrix rate (TFLOP/s): the vendor library's
+    (hipBLASLt, through torch.matmul) n x n x n product."""
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12
+
+
+def peak_probes(torch, dev) -> dict:
+    p_bytes = 151936 * 128 * 2 // 16 * 16
+    rot = math.ceil(2 * MALL_BYTES / p_bytes)
+    return {"hbm_read_gbs": {f"{p_bytes} B x {rot} rotating buffers (P of the headline head, cold)":
+                             probe_hbm_read(torch, dev, p_bytes, rot, 140),
+                             "1 GiB": probe_hbm_read(torch, dev, 1 << 30, 1, 12)},
+            "mfma_bf16_tflops": {"8192^3 torch.matmul (hipBLASLt)": probe_mfma_bf16(torch, dev)},
+            "spec": {"hbm_gbs": HBM_PEAK_GBS, "mfma_tflops": MFMA_PEAK_TFLOPS}}
 
 
 # ------------------------------------------------ latency table and recall
@@ -355,7 +497,10 @@ def main() -> int:
                                    "timed on a single MI355X, with no collectives; the multi-GPU sharding "
                                    "is a design note only. Run with --gpus 1."}), flush=True)
         return 2
-    if args.table or args.recall or args.factor:
+    if args.summarise_counters:
+        print(summarise_counters(*args.summarise_counters, f"c{args.config}", args.copy_calibration_mib or 256))
+        return 0
+    if args.table or args.recall or args.factor or args.peak:
         import torch
         import rank_lm_head_amd as lr
         dev = torch.device("cuda:0")
@@ -364,6 +509,8 @@ def main() -> int:
             res = latency_table(torch, lr, dev, args.steps)
         elif args.recall:
             res = recall_sweep(torch, lr, dev)
+        elif args.peak:
+            res = peak_probes(torch, dev)
         else:
             res = factor_timing(torch, lr, dev)
         print(json.dumps(res), flush=True)
@@ -435,50 +582,63 @@ def main() -> int:
     idx_last = out[0].cpu().numpy()
     U = int(np.unique(idx_last).size)
 
-    # full-head baseline
-    KB = max(1, args.baseline_steps)
-    g_full = capture(torch, full, 4)
-    for _ in range(2):
-        g_full.replay()
-    t_full = timed_graph_replays(torch, g_full, (KB + 3) // 4)
-    us_full = t_full / ((KB + 3) // 4 * 4) * 1e6
-    full_sel_s = event_timed(torch, hip, heads[:1], full, min(KB, 200))
-
-    # vendor context: the library GEMM (hipBLASLt through torch) for all V
-    # logits of the full head on the same rows, without any selection
+    # full-head baseline (and the vendor GEMM's rate beside it)
+    us_full = full_sel_s = None
     vendor = None
-    if cfg.dtype == "bf16":
-        Hb = dsets[0]["H"]
-        lin = torch.nn.functional.linear
+    if not args.draft_only:
+        KB = max(1, args.baseline_steps)
+        g_full = capture(torch, full, 4)
         for _ in range(2):
-            lin(Hb, W)
-        torch.cuda.synchronize()
-        reps = max(2, min(50, int(2e5 // max(1.0, us_full))))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            lin(Hb, W)
-        e1.record()
-        torch.cuda.synchronize()
-        v_us = e0.elapsed_time(e1) / reps * 1e3
-        vendor = {"op": "torch.nn.functional.linear(H, W): all V logits of the full head, bf16 out, no selection",
-                  "us_per_call": v_us, "tflops": 2.0 * cfg.B * cfg.V * cfg.d / v_us / 1e6,
-                  "hbm_frac": (cfg.V * cfg.d * s + cfg.B * cfg.d * s + cfg.B * cfg.V * s) / (v_us * 1e-6)
-                              / (HBM_PEAK_GBS * 1e9)}
+            g_full.replay()
+        t_full = timed_graph_replays(torch, g_full, (KB + 3) // 4)
+        us_full = t_full / ((KB + 3) // 4 * 4) * 1e6
+        full_sel_s = event_timed(torch, hip, heads[:1], full, min(KB, 200))
 
-    # roofline of the dominant kernel: the vocabulary score pass. Algorithmic
-    # work per launch: every P row once (V units of r*s bytes) plus the B rows
-    # of z, and 2*B*r flops per vocabulary row. Small batches stream P on the
-    # vector ALU (HBM-bound); row batches run the matrix-core GEMM, which is
-    # bound by whichever of HBM and MFMA its arithmetic intensity points to.
+        # vendor context: the library GEMM (hipBLASLt through torch) for all V
+        # logits of the full head on the same rows, without any selection
+        vendor = None
+        if cfg.dtype == "bf16":
+            Hb = dsets[0]["H"]
+            lin = torch.nn.functional.linear
+            for _ in range(2):
+                lin(Hb, W)
+            torch.cuda.synchronize()
+            reps = max(2, min(50, int(2e5 // max(1.0, us_full))))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                lin(Hb, W)
+            e1.record()
+            torch.cuda.synchronize()
+            v_us = e0.elapsed_time(e1) / reps * 1e3
+            vendor = {"op": "torch.nn.functional.linear(H, W): all V logits of the full head, bf16 out, no selection",
+                      "us_per_call": v_us, "tflops": 2.0 * cfg.B * cfg.V * cfg.d / v_us / 1e6,
+                      "hbm_frac": (cfg.V * cfg.d * s + cfg.B * cfg.d * s + cfg.B * cfg.V * s) / (v_us * 1e-6)
+                                  / (HBM_PEAK_GBS * 1e9)}
+
+    # roofline of the dominant kernel. Algorithmic work per launch of the
+    # vocabulary score pass: every P row once (V units of r*s bytes) plus the
+    # B rows of z, and 2*B*r flops per vocabulary row. One row of bf16 runs
+    # the whole call after the down-projection in one kernel (draft1_kernel:
+    # scores, selection, merge and rescoring), whose bytes add the k rows of
+    # W it gathers (U distinct) and h. Other small batches stream P on the
+    # vector ALU (HBM-bound); row batches run the matrix-core GEMM, bound by
+    # whichever of HBM and MFMA its arithmetic intensity points to.
     sel_bytes = cfg.V * cfg.r * s + cfg.B * cfg.r * s
     sel_flops = 2.0 * cfg.B * cfg.V * cfg.r
-    small = cfg.dtype == "bf16" and cfg.B <= (4 if cfg.r >= 512 else 8) and cfg.r in (8, 16, 32, 64, 128, 256, 512)
+    pow2_r = cfg.r in (8, 16, 32, 64, 128, 256, 512)
+    small = cfg.dtype == "bf16" and cfg.B <= (4 if cfg.r >= 512 else 8) and pow2_r
+    n_b1 = max(1, min((cfg.V + 63) // 64, N_CU, B1_MAX_BLOCKS))
+    one_row = cfg.dtype == "bf16" and cfg.B == 1 and pow2_r and (cfg.V + n_b1 - 1) // n_b1 <= B1_MAX_ROWS_PER_BLOCK
     batch = cfg.dtype == "bf16" and cfg.B > 4 and not small
     if batch and cfg.r <= 256 and cfg.B > 256:
         sel_kernel, what = "strip_sel_kernel", "main pass: scores of all rows, flagged above the sampled bound"
     elif batch:
         sel_kernel, what = "gemm_sel_kernel", "main GEMM pass: scores of all rows, flagged above the sampled bound"
+    elif one_row:
+        sel_kernel, what = "draft1_kernel", "score stream + per-slice top-k + merge + rescoring of the winners"
+        sel_bytes += (U + 1) * cfg.d * s + cfg.k * 12
+        sel_flops += 2.0 * cfg.k * cfg.d
     elif small:
         sel_kernel, what = "select_short_kernel", "score pass + per-slice top-k"
     else:
@@ -487,15 +647,22 @@ def main() -> int:
     mfma_bound = sel_flops / sel_bytes > peak_flops / (HBM_PEAK_GBS * 1e9)
     traffic = traffic_from_profiles(sel_kernel, f"c{cid}")
     if mfma_bound:
+        ach = probe_mfma_bf16(torch, dev) if cfg.dtype == "bf16" else None
         roof = {"bound": "mfma", "kernel": f"{sel_kernel} ({what})",
                 "achieved": sel_flops / sel_s / 1e12, "peak": peak_flops / 1e12, "unit": "TFLOP/s",
                 "frac": sel_flops / sel_s / peak_flops, "traffic": traffic,
                 "us_per_launch": sel_s * 1e6, "flops_per_launch": sel_flops, "bytes_per_launch": sel_bytes}
+        if ach:
+            roof["achievable"] = {"peak": ach, "frac": sel_flops / sel_s / 1e12 / ach,
+                                  "probe": "8192^3 bf16 torch.matmul (hipBLASLt)"}
     else:
+        ach = probe_hbm_read(torch, dev, (sel_bytes // 16) * 16, max(1, math.ceil(2 * MALL_BYTES / sel_bytes)), 140)
         roof = {"bound": "hbm", "kernel": f"{sel_kernel} ({what})",
                 "achieved": sel_bytes / sel_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": sel_bytes / sel_s / (HBM_PEAK_GBS * 1e9), "traffic": traffic,
-                "us_per_launch": sel_s * 1e6, "bytes_per_launch": sel_bytes}
+                "us_per_launch": sel_s * 1e6, "bytes_per_launch": sel_bytes,
+                "achievable": {"peak": ach, "frac": sel_bytes / sel_s / 1e9 / ach,
+                               "probe": "plain streaming read of the same bytes, cold (csrc/probe_read.hip)"}}
     call_bytes = (cfg.r * cfg.d + cfg.V * cfg.r + cfg.B * cfg.d + U * cfg.d) * s + cfg.B * cfg.k * 12
     call_flops = 2.0 * cfg.B * (cfg.r * cfg.d + cfg.V * cfg.r + cfg.k * cfg.d)
     full_bytes = cfg.V * cfg.d * s + cfg.B * cfg.d * s
@@ -525,12 +692,15 @@ def main() -> int:
         "call_flops": call_flops,
         "distinct_W_rows": U,
         "roofline": roof,
-        "full_head": {"us_per_call": us_full, "speedup_of_draft_head": us_full / us_cold,
-                      "select_us_per_launch": full_sel_s * 1e6,
-                      "hbm_frac": full_bytes / (full_sel_s) / (HBM_PEAK_GBS * 1e9),
-                      "mfma_frac": 2.0 * cfg.B * cfg.V * cfg.d / full_sel_s / peak_flops,
-                      "vendor_gemm_context": vendor},
     }
+    if us_full is not None:
+        line["full_head"] = {"us_per_call": us_full, "speedup_of_draft_head": us_full / us_cold,
+                             "select_us_per_launch": full_sel_s * 1e6,
+                             "hbm_frac": full_bytes / (full_sel_s) / (HBM_PEAK_GBS * 1e9),
+                             "mfma_frac": 2.0 * cfg.B * cfg.V * cfg.d / full_sel_s / peak_flops,
+                             "vendor_gemm_context": vendor}
+        if vendor:
+            line["full_head"]["speedup_of_draft_head_vs_vendor_gemm"] = vendor["us_per_call"] / us_cold
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -540,7 +710,7 @@ def main() -> int:
         torch.cuda.synchronize()
         line["copy_calibration_bytes"] = n
         del src, dst
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.draft_only:
         line["cpu_baseline"] = cpu_baseline(base, args.cpu_seconds)
     for h in heads:
         h.close()

@@ -1,4 +1,5 @@
-"""Builds liblrhead.so in-tree with hipcc for gfx950.
+"""Builds liblrhead.so (and the benchmark's read probe, libprobe.so) in-tree
+with hipcc for gfx950.
 
     python -m rank_lm_head_amd.build
 
@@ -18,6 +19,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "liblrhead.so")
+PROBE_LIB = os.path.join(PKG, "libprobe.so")   # measurement only, not the head's ABI
+PROBE_SOURCE = "probe_read.hip"
 OBJ = os.path.join(PKG, "_build")
 SOURCES = ["kernels_small.hip", "kernels_mfma.hip", "kernels_gemm.hip", "kernels_merge.hip", "kernels_branch.hip",
            "kernels_factor.hip", "kernels_b1.hip", "lrhead.hip"]
@@ -44,9 +47,16 @@ def build(verbose: bool = False) -> str:
     for s in SOURCES:
         obj = os.path.join(OBJ, os.path.splitext(s)[0] + ".o")
         jobs.append((obj, [HIPCC, *FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", obj]))
+    probe_tmp = PROBE_LIB + ".tmp"
+    probe = [HIPCC, *FLAGS, "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_tmp]
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(max_workers=workers) as ex:
+        probe_job = ex.submit(_run, probe)
         results = list(ex.map(lambda j: _run(j[1]), jobs))
+        probe_res = probe_job.result()
+    if probe_res[0] != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(probe) + "\n" + "\n".join(probe_res[1]))
+    os.replace(probe_tmp, PROBE_LIB)
     out = []
     for (obj, cmd), (rc, msgs) in zip(jobs, results):
         if rc != 0:

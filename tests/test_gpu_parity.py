@@ -241,9 +241,15 @@ def test_config_draft_head(cid):
     idx, score, lg = np_(idx), np_(score), np_(lg)
     assert not check_properties(idx, score, cfg.V)
     assert np.all(np.isfinite(lg))
-    rows = _sample_rows(cfg.B)
-    errs, stats = check_lowrank(inp, cfg.k, idx, score, lg, rows=rows)
-    say(f"[ok?] c{cid} rows checked {len(rows)} {stats} errors {len(errs)}")
+    # every row, in chunks that bound the oracle's float64 score block
+    errs, exact, n_rows = [], 0, 0
+    for lo in range(0, cfg.B, 256):
+        rows = np.arange(lo, min(cfg.B, lo + 256))
+        e, stats = check_lowrank(inp, cfg.k, idx, score, lg, rows=rows)
+        errs += e
+        exact += stats["exact_rows"]
+        n_rows += len(rows)
+    say(f"[ok?] c{cid} rows checked {n_rows}, identical to the oracle {exact}, errors {len(errs)}")
     assert not errs, errs[:5]
 
 
