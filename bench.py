@@ -153,29 +153,35 @@ def summarise_counters(fetch_csv: str, write_csv: str, workload: str, calib_mib:
     import csv
 
     def per_kernel(path):
-        acc = {}
+        acc, per_dispatch = {}, {}
         for row in csv.DictReader(open(path)):
             name = row["Kernel_Name"]
-            a = acc.setdefault(name, {"dispatches": set(), "kib": 0.0})
-            a["dispatches"].add(row.get("Dispatch_Id") or row.get("Correlation_Id"))
-            a["kib"] += float(row["Counter_Value"])
-        return {n: (len(a["dispatches"]), a["kib"]) for n, a in acc.items()}
+            key = (name, row.get("Dispatch_Id") or row.get("Correlation_Id"))
+            per_dispatch[key] = per_dispatch.get(key, 0.0) + float(row["Counter_Value"])
+        for (name, _), v in per_dispatch.items():
+            a = acc.setdefault(name, [0, 0.0, 0.0])
+            a[0] += 1
+            a[1] += v
+            a[2] = max(a[2], v)
+        return acc
 
     fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
     cal = calib_mib * 1024.0
-    cf = [v for n, v in fetch.items() if "copyBuffer" in n]
-    cw = [v for n, v in write.items() if "copyBuffer" in n]
-    f_scale = cal / (cf[0][1] / cf[0][0]) if cf else 1.0
-    w_scale = cal / (cw[0][1] / cw[0][0]) if cw else 1.0
+    # the calibration copy is the largest device copy of the run (the others
+    # are the inputs' uploads)
+    cf = [v[2] for n, v in fetch.items() if "copyBuffer" in n]
+    cw = [v[2] for n, v in write.items() if "copyBuffer" in n]
+    f_scale = cal / cf[0] if cf and cf[0] > 0 else 1.0
+    w_scale = cal / cw[0] if cw and cw[0] > 0 else 1.0
     path = os.path.join(ROOT, "profiles", "counters.json")
     allrec = json.load(open(path)) if os.path.exists(path) else {}
     recs = {}
     lines = [f"Calibration: a {calib_mib} MiB device copy; FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}.",
              "", "| Kernel | Dispatches | read MB / launch | written MB / launch |", "|---|---|---|---|"]
-    for name, (nd, kib) in fetch.items():
+    for name, (nd, kib, _) in fetch.items():
         if "copyBuffer" in name:
             continue
-        wk = write.get(name, (nd, 0.0))[1]
+        wk = write.get(name, (nd, 0.0, 0.0))[1]
         rd = kib / nd * 1024 * f_scale
         wr = wk / nd * 1024 * w_scale
         rec = {"dispatches": nd, "read_bytes": rd, "written_bytes": wr, "bytes_per_launch": rd + wr}
