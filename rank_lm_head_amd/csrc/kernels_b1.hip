@@ -34,6 +34,8 @@ namespace lrh {
 constexpr int kDownThreads = 256;
 constexpr int kDieGroups = 8;       // blockIdx % 8: the compute-die of the block
 constexpr int kSyncStride = 32;     // 32-bit words between counters (128 bytes)
+constexpr uint32_t kNoLogit = 0xFFFFFFFFu;   // a speculative logit not written yet (a NaN no dot product gives)
+constexpr int kSpecPolls = 8;                // re-reads of a speculative logit that had not landed
 constexpr int kB1MaxRowsPerBlock = 16 * kWave;
 
 // ------------------------------------------------------------ z = Q . h
@@ -43,16 +45,19 @@ constexpr int kB1MaxRowsPerBlock = 16 * kWave;
 // products); each wave sums its lanes, and thread b adds the four wave sums
 // in a fixed order and rounds to bf16. Chunks past d read a clamped, valid
 // address and are zeroed. Block 0 also zeroes `nsync` counters of the
-// following score pass.
+// following score pass, and the blocks set its n_lgs speculative logits to
+// kNoLogit ("not written yet").
 template <int NB, int NL>
 __global__ void __launch_bounds__(kDownThreads) down_wide_kernel(const uint16_t* __restrict__ Q,
                                                                  const uint16_t* __restrict__ H, int r, int d,
                                                                  int B, uint16_t* __restrict__ Z,
-                                                                 uint32_t* __restrict__ sync, int nsync) {
+                                                                 uint32_t* __restrict__ sync, int nsync,
+                                                                 uint32_t* __restrict__ lgs, int n_lgs) {
   __shared__ float part[kDownThreads / kWave][NB];
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int j = blockIdx.x;
   if (j == 0 && tid < nsync) sync[tid * kSyncStride] = 0u;
+  for (int e = j * kDownThreads + tid; e < n_lgs; e += r * kDownThreads) lgs[e] = kNoLogit;
   const uint16_t* q = Q + (int64_t)j * d;
   float acc[NB];
 #pragma unroll
@@ -122,6 +127,7 @@ struct B1Smem {
   alignas(16) uint64_t cand[kCandSlots];   // candidate keys
   float clog[kCandSlots];       // and their exact logits, where known
   uint8_t chas[kCandSlots];
+  int csrc[kCandSlots];         // where its speculative logit lands (-1: none)
   int deep[kMaxLists];          // lists that may hold more than their entries
   uint64_t deep_key[kMaxLists]; // and the key of their last entry
   uint64_t tmp[kWave];
@@ -131,6 +137,8 @@ struct B1Smem {
   int miss[kWave];              // winners whose logit is still to compute
   int tops[kB1List];            // ids of the slice's best entries
   int rounds_done;              // of wave 0's selection rounds
+  int ready;                    // waves whose list / raw-score stores have completed
+  int decided;                  // the ticket has been taken (m.last is set)
   int n_cand, n_deep, n_miss, last;
 };
 
@@ -147,6 +155,7 @@ __device__ __forceinline__ void b1_push(B1Smem& m, bool ps, uint64_t key) {
     if (ps && slot < kCandSlots) {
       m.cand[slot] = key;
       m.chas[slot] = 0;
+      m.csrc[slot] = -1;
     }
   }
 }
@@ -270,7 +279,8 @@ __device__ __forceinline__ void b1_merge(B1Smem& m, const uint64_t* __restrict__
         if (slot < kCandSlots) {
           m.cand[slot] = key[j];
           m.clog[slot] = lg[j];
-          m.chas[slot] = lgs != nullptr && j < kB1Spec;
+          m.chas[slot] = lgs != nullptr && j < kB1Spec && __float_as_uint(lg[j]) != kNoLogit;
+          m.csrc[slot] = lgs != nullptr && j < kB1Spec ? j * n + p : -1;
         }
         ++slot;
       }
@@ -355,7 +365,11 @@ __global__ void __launch_bounds__(kMergeThreads) draft1_kernel(
   const int nrows = (int)(bhi - blo);
 
   // 1. scores of the slice
-  if (threadIdx.x == 0) m.rounds_done = 0;
+  if (threadIdx.x == 0) {
+    m.rounds_done = 0;
+    m.ready = 0;
+    m.decided = 0;
+  }
   stream_scores<K, 1>(P, Z, 1, blo, wlo, whi, sc, E * kWave);
   __syncthreads();
 
@@ -363,6 +377,7 @@ __global__ void __launch_bounds__(kMergeThreads) draft1_kernel(
   // of the first kB1Spec of them, each started as soon as its round is done
   // (waves 1..kB1Spec wait on an LDS counter, which wave 0 always takes to
   // L); the raw copy (the remaining waves)
+  auto lds_load = [](const int& v) { return __hip_atomic_load(&v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); };
   if (wave == 0) {
     SliceTop<E> st;
     st.load(sc, nrows);
@@ -376,8 +391,8 @@ __global__ void __launch_bounds__(kMergeThreads) draft1_kernel(
     if (lane < L) st_dev<uint64_t>(&keys[lane * n + x], st.my_i != kSentinelId ? cand_key(st.my_s, st.my_i) : 0ull);
   } else if (wave <= kB1Spec) {
     if (rescore && wave <= L) {
-      while (__hip_atomic_load(&m.rounds_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < wave)
-        __builtin_amdgcn_s_sleep(1);
+      while (lds_load(m.rounds_done) < wave) __builtin_amdgcn_s_sleep(1);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       const int v = m.tops[wave - 1];
       if (v != kSentinelId) {
         const float lg = wave_row_dot<uint16_t>(W + (int64_t)v * d, H, d);
@@ -389,10 +404,17 @@ __global__ void __launch_bounds__(kMergeThreads) draft1_kernel(
       st_dev(&raw[blo + j], sc[j]);
   }
 
-  // 3. tickets
-  wait_stores();
-  __syncthreads();
+  // 3. tickets, once the lists and raw scores have landed. The speculative
+  // logits are not waited for: the merge reads them again where they had
+  // not landed (down_wide_kernel reset them to kNoLogit).
+  if (wave != 1 && wave != 2) {
+    wait_stores();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) __hip_atomic_fetch_add(&m.ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
   if (threadIdx.x == 0) {
+    while (lds_load(m.ready) < kMergeWaves - 2) __builtin_amdgcn_s_sleep(1);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const int g = x % kDieGroups;
     const uint32_t in_group = (uint32_t)((n - g + kDieGroups - 1) / kDieGroups);
     const uint32_t groups = (uint32_t)(n < kDieGroups ? n : kDieGroups);
@@ -405,9 +427,13 @@ __global__ void __launch_bounds__(kMergeThreads) draft1_kernel(
       is_last = t2 == groups - 1;
     }
     m.last = is_last;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __hip_atomic_store(&m.decided, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-  __syncthreads();
-  if (!m.last) return;
+  if (lane == 0)
+    while (lds_load(m.decided) == 0) __builtin_amdgcn_s_sleep(1);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (!__builtin_amdgcn_readfirstlane(m.last)) return;   // block-uniform
 
   // 4. the merge, by the last block
   b1_merge(m, keys, rescore ? lgs : nullptr, n, L, L < k ? raw : nullptr, V, k);
@@ -422,7 +448,19 @@ __global__ void __launch_bounds__(kMergeThreads) draft1_kernel(
     const int r = lane;
     const int slot = r < k ? m.top_slot[r] : -1;
     const int v = r < k ? m.top_i[r] : kSentinelId;
-    const bool known = slot >= 0 && m.chas[slot];
+    bool known = slot >= 0 && m.chas[slot];
+    if (slot >= 0 && !known && m.csrc[slot] >= 0) {   // a speculative logit that had not landed yet
+      const int src = m.csrc[slot];
+      for (int polls = 0; polls < kSpecPolls && !known; ++polls) {
+        const float g = ld_dev(&lgs[src]);
+        if (__float_as_uint(g) != kNoLogit) {
+          m.clog[slot] = g;
+          known = true;
+        } else {
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+    }
     const bool need = v != kSentinelId && !known;
     const unsigned long long mk = __ballot(need);
     if (need) m.miss[lanes_below(mk)] = r;
@@ -462,8 +500,9 @@ static int down_wide_loads(int d) {
 }
 
 hipError_t launch_down_wide(const void* Q, const void* H, int r, int d, int64_t B, void* Z, uint32_t* sync,
-                            int nsync, hipStream_t stream) {
-  if (B < 1 || B > kSmallB || nsync > kDownThreads) return hipErrorInvalidValue;
+                            int nsync, float* lgs, int n_lgs, hipStream_t stream) {
+  if (B < 1 || B > kSmallB || nsync > kDownThreads || n_lgs < 0) return hipErrorInvalidValue;
+  uint32_t* lg32 = reinterpret_cast<uint32_t*>(lgs);
   const dim3 grid(r), block(kDownThreads);
   const int nl = down_wide_loads(d);
   const uint16_t* q = (const uint16_t*)Q;
@@ -472,10 +511,10 @@ hipError_t launch_down_wide(const void* Q, const void* H, int r, int d, int64_t 
 #define LRH_DW(NB)                                                                                              \
   do {                                                                                                          \
     switch (nl) {                                                                                               \
-      case 1: hipLaunchKernelGGL((down_wide_kernel<NB, 1>), grid, block, 0, stream, q, h, r, d, (int)B, z, sync, nsync); break; \
-      case 2: hipLaunchKernelGGL((down_wide_kernel<NB, 2>), grid, block, 0, stream, q, h, r, d, (int)B, z, sync, nsync); break; \
-      case 3: hipLaunchKernelGGL((down_wide_kernel<NB, 3>), grid, block, 0, stream, q, h, r, d, (int)B, z, sync, nsync); break; \
-      default: hipLaunchKernelGGL((down_wide_kernel<NB, 4>), grid, block, 0, stream, q, h, r, d, (int)B, z, sync, nsync); break; \
+      case 1: hipLaunchKernelGGL((down_wide_kernel<NB, 1>), grid, block, 0, stream, q, h, r, d, (int)B, z, sync, nsync, lg32, n_lgs); break; \
+      case 2: hipLaunchKernelGGL((down_wide_kernel<NB, 2>), grid, block, 0, stream, q, h, r, d, (int)B, z, sync, nsync, lg32, n_lgs); break; \
+      case 3: hipLaunchKernelGGL((down_wide_kernel<NB, 3>), grid, block, 0, stream, q, h, r, d, (int)B, z, sync, nsync, lg32, n_lgs); break; \
+      default: hipLaunchKernelGGL((down_wide_kernel<NB, 4>), grid, block, 0, stream, q, h, r, d, (int)B, z, sync, nsync, lg32, n_lgs); break; \
     }                                                                                                           \
   } while (0)
   if (B == 1)

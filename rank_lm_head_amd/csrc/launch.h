@@ -49,9 +49,10 @@ hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, in
 
 // ------------------------------------------------------- kernels_b1.hip
 // z = round(Q . h) for B <= kSmallB rows, one block per row of Q; block 0
-// also zeroes nsync completion counters (128 bytes apart) of the next pass.
+// also zeroes nsync completion counters (128 bytes apart) of the next pass,
+// and the blocks mark its n_lgs speculative logits "not written".
 hipError_t launch_down_wide(const void* Q, const void* H, int r, int d, int64_t B, void* Z, uint32_t* sync,
-                            int nsync, hipStream_t stream);
+                            int nsync, float* lgs, int n_lgs, hipStream_t stream);
 // The one-row call in one pass after the down-projection: score stream,
 // slice lists, the speculative logit of each slice's best entry, and the
 // merge with the remaining logits in the pass's last block.

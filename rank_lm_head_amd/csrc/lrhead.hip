@@ -162,7 +162,8 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   if (lrh::b1_path(h->dtype, B, h->r, h->V, h->n_cu)) {
     // one row: the down-projection (which also resets the pass's counters),
     // then a single pass that scores, selects, merges and rescores
-    LRH_HIP(lrh::launch_down_wide(h->Q, H, (int)h->r, (int)h->d, B, h->z, h->sync, lrh::kB1Counters, s),
+    LRH_HIP(lrh::launch_down_wide(h->Q, H, (int)h->r, (int)h->d, B, h->z, h->sync, lrh::kB1Counters, h->b1_lgs,
+                                  2 * lrh::b1_blocks(h->V, h->n_cu), s),
             "down-projection launch");
     lrh::B1Args a;
     a.P = h->P;
@@ -209,7 +210,8 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   int n_lists, list_len = k;
   const float* raw = nullptr;
   if (streaming) {
-    LRH_HIP(lrh::launch_down_wide(h->Q, H, (int)h->r, (int)h->d, B, h->z, nullptr, 0, s), "down-projection launch");
+    LRH_HIP(lrh::launch_down_wide(h->Q, H, (int)h->r, (int)h->d, B, h->z, nullptr, 0, nullptr, 0, s),
+            "down-projection launch");
     LRH_HIP(lrh::launch_select_small(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, h->raw, s,
                                      timing(h)),
             "score/selection launch");
