@@ -48,9 +48,11 @@ hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, in
                               int* part_i, hipStream_t stream, Timing t = {});
 
 // ------------------------------------------------------- kernels_b1.hip
-// z = round(Q . h) for B <= kSmallB rows, one block per row of Q; block 0
+// z = round(Q . h) for B <= kDownWideMaxB rows, one block per row of Q and
+// group of 8 rows; block 0
 // also zeroes nsync completion counters (128 bytes apart) of the next pass,
 // and the blocks mark its n_lgs speculative logits "not written".
+constexpr int kDownWideMaxB = 64;
 hipError_t launch_down_wide(const void* Q, const void* H, int r, int d, int64_t B, void* Z, uint32_t* sync,
                             int nsync, float* lgs, int n_lgs, hipStream_t stream);
 // The one-row call in one pass after the down-projection: score stream,

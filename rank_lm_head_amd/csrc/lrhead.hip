@@ -188,14 +188,19 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   }
   const bool streaming = lrh::small_path(h->dtype, B, h->r, h->V);
   if (!streaming && lrh::batch_path(h->dtype, B)) {
-    // many rows: the down-projection is a GEMM worth the pipelined kernel
-    // The sparse score array is written only later in the call, so the
+    // many rows. Up to 64 rows the down-projection takes one block per row
+    // of Q and group of 8 rows (one launch); above that it is a GEMM worth
+    // the pipelined kernel. The sparse score array is written only later in
+    // the call, so the
     // split down-projection keeps its partial sums there when they fit.
     // Measured crossover: the split kernel is faster up to B * r = 65536
     // (B = 256 at r = 256: 144 against 149 us per call; B = 512 at r = 256:
     // 219 against 209 us).
     const size_t part_bytes = size_t(lrh::down_split_parts((int)h->d)) * size_t(B) * size_t(h->r) * 4;
-    if (B >= kDownGemmRows && B * h->r > kDownSplitMaxElems)
+    if (B <= lrh::kDownWideMaxB)
+      LRH_HIP(lrh::launch_down_wide(h->Q, H, (int)h->r, (int)h->d, B, h->z, nullptr, 0, nullptr, 0, s),
+              "down-projection launch");
+    else if (B >= kDownGemmRows && B * h->r > kDownSplitMaxElems)
       LRH_HIP(lrh::launch_down_gemm(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
     else if (part_bytes <= h->bw.S_bytes)
       LRH_HIP(lrh::launch_down_split(h->Q, H, (int)h->r, (int)h->d, B, h->z, h->bw.S, s), "down-projection launch");
