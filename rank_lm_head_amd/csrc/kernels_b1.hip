@@ -157,6 +157,7 @@ struct B1Smem {
   float top_s[kWave];
   int top_i[kWave];
   int top_slot[kWave];          // candidate slot of each winner (-1: none)
+  int rank[kWave];              // partial ranks of the first 64 candidates
   int miss[kWave];              // winners whose logit is still to compute
   int tops[kB1List];            // ids of the slice's best entries
   int rounds_done;              // of wave 0's selection rounds
@@ -245,6 +246,7 @@ __device__ __forceinline__ void b1_merge(B1Smem& m, const uint64_t* __restrict__
     }
   }
   if (threadIdx.x < kHistBins) m.hist[threadIdx.x] = 0;
+  if (threadIdx.x < kWave) m.rank[threadIdx.x] = 0;
   if (threadIdx.x == 0) {
     m.n_cand = 0;
     m.n_deep = 0;
@@ -338,7 +340,33 @@ __device__ __forceinline__ void b1_merge(B1Smem& m, const uint64_t* __restrict__
     __syncthreads();
   }
   const int nc = m.n_cand;
-  if (nc <= kCandSlots) {
+  if (nc <= kWave) {
+    // rank of each candidate: the candidates that precede it, counted for
+    // candidate `lane` by every wave over its eight (w * 8 .. w * 8 + 7)
+    const uint64_t mine = lane < nc ? m.cand[lane] : 0ull;
+    const u64x2* c2 = reinterpret_cast<const u64x2*>(m.cand + 8 * wave);
+    int part = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u64x2 c = c2[j];
+      part += (8 * wave + 2 * j < nc && c.x > mine) + (8 * wave + 2 * j + 1 < nc && c.y > mine);
+    }
+    if (lane < nc && part) atomicAdd(&m.rank[lane], part);
+    __syncthreads();
+    if (wave == 0) {
+      const int r = lane < nc ? m.rank[lane] : kWave;
+      if (r < k) {
+        m.top_s[r] = key_score(mine);
+        m.top_i[r] = key_id(mine);
+        m.top_slot[r] = lane;
+      }
+      if (lane >= nc && lane < k) {   // fewer than k candidates: empty ranks
+        m.top_s[lane] = neg_inf();
+        m.top_i[lane] = kSentinelId;
+        m.top_slot[lane] = -1;
+      }
+    }
+  } else if (nc <= kCandSlots) {
     // rank of each candidate: the candidates that precede it
     if (p < nc) {
       const uint64_t mine = m.cand[p];
