@@ -20,7 +20,11 @@
 //                   (bf16) or an fp32 panel, read as is (M x K) or transposed
 //                   (stored K x M); long K runs as split-K partials
 //   reduce_kernel   sums the split-K partials
-//   chol_kernel     Cholesky of an n x n Gram matrix, one block, fp64
+//   chol_panel_kernel / chol_update_kernel
+//                   blocked right-looking Cholesky of the n x n Gram matrix
+//                   in fp64: per 32-column panel, its diagonal block
+//                   factored in LDS, the rows below it solved one per thread,
+//                   then the trailing lower triangle updated in 64 x 64 tiles
 //   trinv_kernel    the rows of L^-T (= columns of L^-1), one wave per
 //                   column, forward substitution, written as fp32
 //   cast kernels    P and Q in bf16 (Q transposed from W^T . Y)
@@ -131,40 +135,134 @@ __global__ void __launch_bounds__(256) reduce_kernel(const ACC* __restrict__ par
   }
 }
 
-// In place: the lower triangle of G (n x n, row-major, symmetric) becomes L
-// with G = L L^T (right-looking, one column per step, two barriers a step:
-// every thread takes the pivot itself, scales its rows of the column and
-// copies them to LDS; after a barrier the trailing lower triangle is
-// updated from the LDS copy). A pivot that is not positive (a rank-deficient
-// panel) is replaced by a tiny one and counted in *status.
-constexpr int kCholThreads = 1024;
+// In place, the lower triangle of G (n x n, row-major, symmetric) becomes L
+// with G = L L^T, 32 columns at a time (right-looking, blocked):
+//  chol_panel_kernel  every block copies the diagonal block G[k0.., k0..]
+//                     (32 x 32) to LDS and factors it there, one column per
+//                     step (pivot, scale the column, update the trailing
+//                     triangle); block 0 writes it back. Then each thread
+//                     takes one row i below the block and solves
+//                     x . L11^T = G[i, k0..] by forward substitution, with
+//                     the row in registers;
+//  chol_update_kernel G[i, c] -= sum_l L[i, k0 + l] L[c, k0 + l] for the
+//                     trailing rows and columns c <= i, one 64 x 64 tile of
+//                     the lower triangle per block, 4 x 4 outputs per thread.
+// A pivot that is not positive (a rank-deficient panel) is replaced by a tiny
+// one and counted in *status.
 constexpr int kCholMax = 512;
-__global__ void __launch_bounds__(kCholThreads) chol_kernel(double* __restrict__ G, int n,
-                                                           uint32_t* __restrict__ status) {
-  __shared__ double col[kCholMax];
-  for (int j = 0; j < n; ++j) {
-    double d = G[(int64_t)j * n + j];
+constexpr int kCholNb = 32;
+constexpr int kCholRows = 256;   // rows below the diagonal block per panel block
+constexpr int kCholTile = 64;
+
+__global__ void __launch_bounds__(kCholRows) chol_panel_kernel(double* __restrict__ G, int n, int k0,
+                                                               uint32_t* __restrict__ status) {
+  __shared__ double a[kCholNb][kCholNb + 1];
+  const int tid = threadIdx.x;
+  const int nb = min(kCholNb, n - k0);
+  for (int t = tid; t < nb * nb; t += kCholRows) {
+    const int i = t / nb, c = t % nb;
+    a[i][c] = c <= i ? G[(int64_t)(k0 + i) * n + k0 + c] : 0.0;
+  }
+  __syncthreads();
+  for (int j = 0; j < nb; ++j) {
+    double d = a[j][j];
     if (!(d > 0.0)) {
-      if (threadIdx.x == 0) atomicAdd(status, 1u);
+      if (blockIdx.x == 0 && tid == 0) atomicAdd(status, 1u);
       d = 1e-300;
     }
     const double piv = sqrt(d);
-    for (int i = j + 1 + threadIdx.x; i < n; i += kCholThreads) {
-      const double v = G[(int64_t)i * n + j] / piv;
-      G[(int64_t)i * n + j] = v;
-      col[i] = v;
-    }
+    __syncthreads();   // every thread has read the old diagonal
+    if (tid == 0) a[j][j] = piv;
+    if (tid > j && tid < nb) a[tid][j] /= piv;
     __syncthreads();
-    if (threadIdx.x == 0) G[(int64_t)j * n + j] = piv;   // every thread has read the old diagonal
-    // trailing update of the lower triangle: rows i > j, columns j < c <= i
-    // (32-bit indices: n <= 512)
-    const int m = n - j - 1;
-    for (int t = threadIdx.x; t < m * m; t += kCholThreads) {
+    const int m = nb - j - 1;
+    for (int t = tid; t < m * m; t += kCholRows) {
       const int i = j + 1 + t / m, c = j + 1 + t % m;
-      if (c <= i) G[i * n + c] -= col[i] * col[c];
+      if (c <= i) a[i][c] -= a[i][j] * a[c][j];
     }
     __syncthreads();
   }
+  if (blockIdx.x == 0)
+    for (int t = tid; t < nb * nb; t += kCholRows) {
+      const int i = t / nb, c = t % nb;
+      if (c <= i) G[(int64_t)(k0 + i) * n + k0 + c] = a[i][c];
+    }
+  const int i = k0 + nb + blockIdx.x * kCholRows + tid;
+  if (i >= n) return;
+  double x[kCholNb];
+  double* row = G + (int64_t)i * n + k0;
+#pragma unroll
+  for (int j = 0; j < kCholNb; ++j) x[j] = j < nb ? row[j] : 0.0;
+#pragma unroll
+  for (int j = 0; j < kCholNb; ++j) {
+    if (j < nb) {
+      double s = x[j];
+#pragma unroll
+      for (int l = 0; l < j; ++l) s -= x[l] * a[j][l];
+      x[j] = s / a[j][j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kCholNb; ++j)
+    if (j < nb) row[j] = x[j];
+}
+
+__global__ void __launch_bounds__(256) chol_update_kernel(double* __restrict__ G, int n, int k0) {
+  __shared__ double li[kCholTile][kCholNb + 1], lc[kCholTile][kCholNb + 1];
+  const int r0 = k0 + kCholNb;   // first trailing row and column
+  // block -> tile (ti, tc) of the lower triangle, tc <= ti
+  int ti = 0, rem = blockIdx.x;
+  while (rem > ti) {
+    rem -= ti + 1;
+    ++ti;
+  }
+  const int tc = rem;
+  const int i0 = r0 + ti * kCholTile, c0 = r0 + tc * kCholTile;
+  const int tid = threadIdx.x;
+  for (int t = tid; t < kCholTile * kCholNb; t += 256) {
+    const int rr = t / kCholNb, l = t % kCholNb;
+    li[rr][l] = i0 + rr < n ? G[(int64_t)(i0 + rr) * n + k0 + l] : 0.0;
+    lc[rr][l] = c0 + rr < n ? G[(int64_t)(c0 + rr) * n + k0 + l] : 0.0;
+  }
+  __syncthreads();
+  const int ty = tid / 16, tx = tid % 16;   // rows ty + 16 u, columns tx + 16 v
+  double acc[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+#pragma unroll 8
+  for (int l = 0; l < kCholNb; ++l) {
+    double xa[4], xb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) xa[u] = li[ty + 16 * u][l];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xb[v] = lc[tx + 16 * v][l];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[u][v] += xa[u] * xb[v];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = i0 + ty + 16 * u, c = c0 + tx + 16 * v;
+      if (i < n && c <= i) G[(int64_t)i * n + c] -= acc[u][v];
+    }
+}
+
+hipError_t cholesky(double* G, int n, uint32_t* status, hipStream_t s) {
+  for (int k0 = 0; k0 < n; k0 += kCholNb) {
+    const int below = n - k0 - kCholNb;
+    const int blocks = below > 0 ? (below + kCholRows - 1) / kCholRows : 1;
+    hipLaunchKernelGGL(chol_panel_kernel, dim3((unsigned)blocks), dim3(kCholRows), 0, s, G, n, k0, status);
+    if (below > 0) {
+      const int T = (below + kCholTile - 1) / kCholTile;
+      hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(T * (T + 1) / 2)), dim3(256), 0, s, G, n, k0);
+    }
+  }
+  return hipGetLastError();
 }
 
 // Rinv = L^-T (fp32), n x n row-major. Wave c solves L x = e_c by forward
@@ -303,8 +401,7 @@ hipError_t orth(float*& X, float*& T, int64_t rows, int r, const FactorWs& w, hi
     hipLaunchKernelGGL(reduce_kernel<double>, dim3((unsigned)(((int64_t)r * r + 255) / 256)), dim3(256), 0, s,
                        w.partd, Sz, (int64_t)r * r, w.G);
     LRH_F(hipGetLastError());
-    hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(kCholThreads), 0, s, w.G, r, w.status);
-    LRH_F(hipGetLastError());
+    LRH_F(cholesky(w.G, r, w.status, s));
     hipLaunchKernelGGL(trinv_kernel, dim3((unsigned)((r + kInvWaves - 1) / kInvWaves)), dim3(kInvWaves * 64), 0, s,
                        w.G, r, w.Rinv);
     LRH_F(hipGetLastError());

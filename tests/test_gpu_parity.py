@@ -387,7 +387,7 @@ def test_ties_inside_one_slice_go_to_the_lower_ids(B):
     (20000, 512, 128, 8, "bf16", False),   # eight-row streaming path
     (20000, 512, 128, 8, "bf16", True),    # eight rows, boundary ties
     (4096, 256, 32, 1, "fp32", False),     # fp32 (matrix-core slice lists and merge)
-    (20000, 512, 128, 40, "bf16", False),  # staged GEMM passes, split down-projection
+    (20000, 512, 128, 40, "bf16", False),  # staged GEMM passes, down-projection in 8-row groups
     (20000, 512, 128, 300, "bf16", False), # strip kernel (two batch tiles), split down-projection in the score scratch
 ])
 def test_repeat_calls_and_poisoned_workspace_are_bitwise_stable(V, d, r, B, dt, ties):
