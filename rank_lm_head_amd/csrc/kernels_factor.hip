@@ -124,6 +124,120 @@ __global__ void __launch_bounds__(kGemmThreads) fgemm_kernel(const TA* __restric
   }
 }
 
+// The same product for N >= 128 on 128 x 128 tiles of C: 8 x 8 outputs per
+// thread (16 LDS reads per 64 multiply-adds instead of 8 per 16), and the
+// operand tiles loaded 16 bytes at a time (8 bf16 or 4 fp32 elements of a
+// contiguous run): op(A)'s run is along K (AT = false) or along M (AT =
+// true), B's along N. Requires lda and ldb to be multiples of 8 (bf16) or 4
+// (fp32) and 16-byte aligned rows; runs past the matrix are zero-filled.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBig = 128;
+constexpr int kBigK = 16;
+template <typename TA, bool AT, typename ACC>
+__global__ void __launch_bounds__(kGemmThreads) fgemm_big_kernel(const TA* __restrict__ A, int64_t lda,
+                                                                 const float* __restrict__ Bm, int64_t ldb,
+                                                                 ACC* __restrict__ C, int M, int N, int64_t K,
+                                                                 int64_t kchunk) {
+  constexpr int PA = 16 / sizeof(TA);   // elements of A per 16-byte load
+  __shared__ ACC As[kBigK][kBig + 4];
+  __shared__ ACC Bs[kBigK][kBig + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;   // outputs rows ty * 8 + i, columns tx * 8 + j
+  const int m0 = blockIdx.x * kBig, n0 = blockIdx.y * kBig;
+  const int64_t kb = (int64_t)blockIdx.z * kchunk;
+  const int64_t ke = kb + kchunk < K ? kb + kchunk : K;
+  ACC acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0;
+  for (int64_t k0 = kb; k0 < ke; k0 += kBigK) {
+    // A tile: kBigK x kBig values of op(A)
+    constexpr int NA = kBigK * kBig / PA / kGemmThreads;   // 16-byte loads per thread
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+      const int e = q * kGemmThreads + tid;
+      float v[PA];
+      if (!AT) {   // run along K: row mm, columns kk .. kk + PA
+        const int mm = e / (kBigK / PA), kk = (e % (kBigK / PA)) * PA;
+        const int gm = m0 + mm;
+        const int64_t gk = k0 + kk;
+        if (gm < M && gk + PA <= ke) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(A + (int64_t)gm * lda + gk);
+#pragma unroll
+          for (int u = 0; u < PA; ++u) v[u] = sizeof(TA) == 2 ? __uint_as_float(u % 2 ? w[u / 2] & 0xFFFF0000u : w[u / 2] << 16)
+                                                              : __uint_as_float(w[u]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < PA; ++u) v[u] = gm < M && gk + u < ke ? ld_f32<TA>(A + (int64_t)gm * lda + gk + u) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < PA; ++u) As[kk + u][mm] = (ACC)v[u];
+      } else {     // run along M: row kk of the stored matrix, columns mm .. mm + PA
+        const int kk = e / (kBig / PA), mm = (e % (kBig / PA)) * PA;
+        const int64_t gk = k0 + kk;
+        const int gm = m0 + mm;
+        if (gk < ke && gm + PA <= M) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(A + gk * lda + gm);
+#pragma unroll
+          for (int u = 0; u < PA; ++u) v[u] = sizeof(TA) == 2 ? __uint_as_float(u % 2 ? w[u / 2] & 0xFFFF0000u : w[u / 2] << 16)
+                                                              : __uint_as_float(w[u]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < PA; ++u) v[u] = gk < ke && gm + u < M ? ld_f32<TA>(A + gk * lda + gm + u) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < PA; ++u) As[kk][mm + u] = (ACC)v[u];
+      }
+    }
+    // B tile: kBigK x kBig fp32, runs of 4 along N
+    constexpr int NB = kBigK * kBig / 4 / kGemmThreads;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int e = q * kGemmThreads + tid;
+      const int kk = e / (kBig / 4), nn = (e % (kBig / 4)) * 4;
+      const int64_t gk = k0 + kk;
+      const int gn = n0 + nn;
+      float v[4];
+      if (gk < ke && gn + 4 <= N) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(Bm + gk * ldb + gn);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = __uint_as_float(w[u]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = gk < ke && gn + u < N ? Bm[gk * ldb + gn + u] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Bs[kk][nn + u] = (ACC)v[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kBigK; ++kk) {
+      ACC a[8], b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = As[kk][ty * 8 + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) b[j] = Bs[kk][tx * 8 + j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
+  }
+  ACC* Cz = C + (int64_t)blockIdx.z * M * N;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + ty * 8 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + tx * 8 + j;
+      if (n < N) Cz[(int64_t)m * N + n] = acc[i][j];
+    }
+  }
+}
+
 // out[i] = sum over z < S of part[z * count + i]
 template <typename ACC>
 __global__ void __launch_bounds__(256) reduce_kernel(const ACC* __restrict__ part, int S, int64_t count,
@@ -374,6 +488,15 @@ hipError_t gemm(const TA* A, int64_t lda, const float* B, int64_t ldb, ACC* C, i
                 hipStream_t s) {
   const int64_t kchunk = ((K + S - 1) / S + kTk - 1) / kTk * kTk;
   const int Sz = (int)((K + kchunk - 1) / kchunk);
+  constexpr int PA = 16 / sizeof(TA);
+  const bool aligned = lda % PA == 0 && ldb % 4 == 0 && (reinterpret_cast<uintptr_t>(A) & 15u) == 0 &&
+                       (reinterpret_cast<uintptr_t>(B) & 15u) == 0;
+  if (N >= kBig && aligned) {
+    dim3 grid((unsigned)((M + kBig - 1) / kBig), (unsigned)((N + kBig - 1) / kBig), (unsigned)Sz);
+    hipLaunchKernelGGL((fgemm_big_kernel<TA, AT, ACC>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, C, M, N, K,
+                       kchunk);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((M + kTile - 1) / kTile), (unsigned)((N + kTile - 1) / kTile), (unsigned)Sz);
   hipLaunchKernelGGL((fgemm_kernel<TA, AT, ACC>), grid, dim3(kGemmThreads), 0, s, A, lda, B, ldb, C, M, N, K, kchunk);
   return hipGetLastError();
