@@ -627,13 +627,13 @@ def main() -> int:
     # B rows of z, and 2*B*r flops per vocabulary row. One row of bf16 runs
     # the whole call after the down-projection in one kernel (draft1_kernel:
     # scores, selection, merge and rescoring), whose bytes add the k rows of
-    # W it gathers (U distinct) and h. Other small batches stream P on the
-    # vector ALU (HBM-bound); row batches run the matrix-core GEMM, bound by
+    # W it gathers (U distinct) and h. Other small batches stream P once
+    # (HBM-bound); row batches run the matrix-core GEMM, bound by
     # whichever of HBM and MFMA its arithmetic intensity points to.
     sel_bytes = cfg.V * cfg.r * s + cfg.B * cfg.r * s
     sel_flops = 2.0 * cfg.B * cfg.V * cfg.r
     pow2_r = cfg.r in (8, 16, 32, 64, 128, 256, 512)
-    small = cfg.dtype == "bf16" and cfg.B <= (4 if cfg.r >= 512 else 8) and pow2_r
+    small = cfg.dtype == "bf16" and cfg.B <= 8 and pow2_r
     n_b1 = max(1, min((cfg.V + 63) // 64, N_CU, B1_MAX_BLOCKS))
     one_row = cfg.dtype == "bf16" and cfg.B == 1 and pow2_r and (cfg.V + n_b1 - 1) // n_b1 <= B1_MAX_ROWS_PER_BLOCK
     batch = cfg.dtype == "bf16" and cfg.B > 4 and not small

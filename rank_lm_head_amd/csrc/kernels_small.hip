@@ -4,11 +4,14 @@
 // With one to eight rows both contractions are matrix-vector products and
 // the time is HBM streaming ("EAGLE-4", section "Retrieve vocabulary
 // candidates cheaply, then score them exactly": the low-rank head still
-// scores every vocabulary row, so P is read once per call). Matrix cores
-// would leave 15 of their 16 columns idle here, so these kernels use the
-// vector ALU (bf16 widened to fp32, fp32 FMAs) and spend their effort on
-// the memory side: every wave load is 64 lanes x 16 contiguous bytes, and
-// each wave keeps several loads in flight.
+// scores every vocabulary row, so P is read once per call). The effort goes
+// to the memory side (large loads, several in flight per wave). The
+// arithmetic is still not free: widening every bf16 element and
+// multiplying it once per row on the vector ALU made the 8-row score pass
+// take 22 us against about 10 for its bytes. So with 2 to 8 rows and r >= 32
+// the scores come from the matrix cores (stream_scores_mfma: half of each
+// 16-column tile idle at 8 rows, which costs nothing here); one row, and
+// the full-head rows, stay on the vector ALU.
 //
 //   select_short_kernel s = P . z with the fused k-best of each block's
 //                       slice, for r <= 512 (a power of two)
@@ -91,7 +94,10 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
   const int64_t blo = v32 * blockIdx.x / n32, bhi = v32 * (blockIdx.x + 1) / n32;
   const int64_t wlo = blo + (bhi - blo) * wave / kWavesSmall;
   const int64_t whi = blo + (bhi - blo) * (wave + 1) / kWavesSmall;
-  stream_scores<K, NB>(M, X, B, blo, wlo, whi, &sc[0][0], E * kWave);
+  if constexpr (NB >= 2 && K >= 32)
+    stream_scores_mfma<K, NB>(M, X, B, blo, wlo, whi, &sc[0][0], E * kWave);
+  else
+    stream_scores<K, NB>(M, X, B, blo, wlo, whi, &sc[0][0], E * kWave);
   __syncthreads();
   const int nrows = (int)(bhi - blo);
   if (B < kWavesSmall) {
@@ -185,9 +191,10 @@ int small_blocks(int64_t V) {
 }
 
 bool small_path(int dtype, int64_t B, int64_t K_lowrank, int64_t V) {
-  // rank-512 rows are long enough that from five rows on the matrix-core
-  // path is faster (measured: 77 against 107 us per call for eight rows)
-  if (dtype != 0 || B > (K_lowrank >= 512 ? kLongB : kSmallB)) return false;
+  // (rank-512 rows of five to eight rows once took the matrix-core path:
+  // 77 against 107 us per call for eight rows while this pass multiplied on
+  // the vector ALU; on the matrix cores it is the faster one)
+  if (dtype != 0 || B > kSmallB) return false;
   if (V > (int64_t)kMaxSmallBlocks * kBlockRows) return false;   // rows per block
   return K_lowrank >= 8 && K_lowrank <= 512 && (K_lowrank & (K_lowrank - 1)) == 0;
 }

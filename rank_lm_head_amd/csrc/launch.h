@@ -24,9 +24,10 @@ struct Timing {
       hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);                         \
   } while (0)
 
-// Draft calls with up to kSmallB rows (kLongB at rank 512), and full-head
-// calls with up to kLongB rows, use the streaming (vector ALU) kernels of
-// kernels_small.hip; larger bf16 batches use the matrix-core kernels.
+// Draft calls with up to kSmallB rows, and full-head calls with up to kLongB
+// rows, use the streaming kernels of kernels_small.hip (one pass over P or
+// W; the draft scores of 2-8 rows on the matrix cores, the rest on the
+// vector ALU); larger bf16 batches use the tiled matrix-core kernels.
 constexpr int kSmallB = 8;
 constexpr int kLongB = 4;
 

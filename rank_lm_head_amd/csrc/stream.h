@@ -83,4 +83,74 @@ __device__ __forceinline__ void stream_scores(const uint16_t* __restrict__ M, co
   }
 }
 
+// The same scores on the matrix cores, for 2 to 8 rows (K >= 32): one
+// v_mfma_f32_16x16x32_bf16 multiplies 16 rows of M by the rows of X (padded
+// to 16 with zeros) over 32 of K, so the vector ALU no longer widens and
+// multiplies every element once per row. Lane l supplies row l & 15 of the
+// 16-row tile and chunk l >> 4 (8 elements) of each 32-deep step; output q
+// of lane l is the score of tile row 4 (l >> 4) + q for row l & 15 of X.
+// X's fragments stay in registers for the whole pass. The wave's rows go in
+// tiles of 16, two groups of about 8 wave loads in flight (non-temporal);
+// rows past the wave's range are loaded from its last row and never kept.
+template <int K, int NB>
+__device__ __forceinline__ void stream_scores_mfma(const uint16_t* __restrict__ M, const uint16_t* __restrict__ X,
+                                                   int B, int64_t blo, int64_t wlo, int64_t whi, float* sc,
+                                                   int ldsc) {
+  static_assert(K % 32 == 0 && NB <= 16, "k steps of 32, at most 16 rows of X");
+  constexpr int KS = K / 32;                         // k steps per tile
+  constexpr int TG = KS >= 8 ? 1 : 8 / KS;           // tiles per group
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+  u32x4 xb[KS];
+#pragma unroll
+  for (int t = 0; t < KS; ++t)
+    xb[t] = col < B && col < NB ? load16(X + (int64_t)col * K + t * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+  const int64_t last = whi > 0 ? whi - 1 : 0;
+  const int ng = wlo < whi ? (int)((whi - wlo + 16 * TG - 1) / (16 * TG)) : 0;
+  u32x4 buf0[TG][KS], buf1[TG][KS];
+  auto issue = [&](u32x4 (&buf)[TG][KS], int64_t base) {
+#pragma unroll
+    for (int u = 0; u < TG; ++u) {
+      const int64_t row = base + u * 16 + col;
+      const uint16_t* m = M + (row < last ? row : last) * K + g * 8;
+#pragma unroll
+      for (int t = 0; t < KS; ++t) buf[u][t] = load16_stream(m + t * 32);
+    }
+  };
+  auto consume = [&](const u32x4 (&buf)[TG][KS], int64_t base) {
+#pragma unroll
+    for (int u = 0; u < TG; ++u) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < KS; ++t)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[u][t]),
+                                                      __builtin_bit_cast(bf16x8, xb[t]), acc, 0, 0, 0);
+      if (col < B && col < NB) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t row = base + u * 16 + 4 * g + q;
+          if (row < whi) sc[col * ldsc + (row - blo)] = acc[q];
+        }
+      }
+    }
+  };
+  issue(buf0, wlo);
+  int gi = 0;
+  for (; gi + 2 < ng; gi += 2) {   // buf0 holds group gi on entry
+    const int64_t base = wlo + (int64_t)gi * 16 * TG;
+    issue(buf1, base + 16 * TG);
+    consume(buf0, base);
+    issue(buf0, base + 32 * TG);
+    consume(buf1, base + 16 * TG);
+  }
+  if (gi + 1 < ng) {
+    const int64_t base = wlo + (int64_t)gi * 16 * TG;
+    issue(buf1, base + 16 * TG);
+    consume(buf0, base);
+    consume(buf1, base + 16 * TG);
+  } else if (gi < ng) {
+    consume(buf0, wlo + (int64_t)gi * 16 * TG);
+  }
+}
+
 }  // namespace lrh
