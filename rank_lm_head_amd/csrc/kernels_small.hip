@@ -11,7 +11,10 @@
 // take 22 us against about 10 for its bytes. So with 2 to 8 rows and r >= 32
 // the scores come from the matrix cores (stream_scores_mfma: half of each
 // 16-column tile idle at 8 rows, which costs nothing here); one row, and
-// the full-head rows, stay on the vector ALU.
+// the full-head rows, stay on the vector ALU. (The one-row pass on the
+// matrix cores measured slower, 18.7 against 17.3 us per call at r = 128:
+// its operand tiles turn each 1 KiB wave load into 16 pieces of 64 bytes,
+// and with one row the pass is bound by the memory side alone.)
 //
 //   select_short_kernel s = P . z with the fused k-best of each block's
 //                       slice, for r <= 512 (a power of two)
