@@ -46,6 +46,7 @@ _CSRC = "rank_lm_head_amd/csrc/"
 KERNEL_SOURCES = {
     name: [_CSRC + f for f in srcs + ("topk.h", "device.h", "launch.h")]
     for name, srcs in (("select_short_kernel", ("kernels_small.hip", "stream.h")),
+                       ("select_rows_kernel", ("kernels_small.hip", "stream.h")),
                        ("select_mfma_kernel", ("kernels_mfma.hip",)),
                        ("gemm_sel_kernel", ("kernels_gemm.hip",)), ("strip_sel_kernel", ("kernels_gemm.hip",)),
                        ("draft1_kernel", ("kernels_b1.hip", "merge.h", "stream.h")))
@@ -636,7 +637,10 @@ def main() -> int:
     small = cfg.dtype == "bf16" and cfg.B <= 8 and pow2_r
     n_b1 = max(1, min((cfg.V + 63) // 64, N_CU, B1_MAX_BLOCKS))
     one_row = cfg.dtype == "bf16" and cfg.B == 1 and pow2_r and (cfg.V + n_b1 - 1) // n_b1 <= B1_MAX_ROWS_PER_BLOCK
-    batch = cfg.dtype == "bf16" and cfg.B > 4 and not small
+    col_tile = 16 if cfg.B <= 16 else 32 if cfg.B <= 32 else 64
+    rows = (cfg.dtype == "bf16" and 8 < cfg.B <= 64 and cfg.r in (32, 64, 128, 256, 512)
+            and col_tile * cfg.r <= 16 * 512 and cfg.V <= 512 * 512)
+    batch = cfg.dtype == "bf16" and cfg.B > 4 and not small and not rows
     if batch and cfg.r <= 256 and cfg.B > 256:
         sel_kernel, what = "strip_sel_kernel", "main pass: scores of all rows, flagged above the sampled bound"
     elif batch:
@@ -647,6 +651,8 @@ def main() -> int:
         sel_flops += 2.0 * cfg.k * cfg.d
     elif small:
         sel_kernel, what = "select_short_kernel", "score pass + per-slice top-k"
+    elif rows:
+        sel_kernel, what = "select_rows_kernel", "matrix-core score pass + per-slice best 4 kept in registers"
     else:
         sel_kernel, what = "select_mfma_kernel", "score pass + per-slice top-k"
     peak_flops = MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12

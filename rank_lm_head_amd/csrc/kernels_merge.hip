@@ -63,8 +63,9 @@ __global__ void __launch_bounds__(256) rescore_kernel(const T* __restrict__ W, c
 template <typename T, bool RESCORE>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
     const float* __restrict__ part_s, const int* __restrict__ part_i, int n, int L, const float* __restrict__ raw,
-    int64_t V, int k, const T* __restrict__ W, const T* __restrict__ H, int d, int32_t* __restrict__ idx,
-    float* __restrict__ score, float* __restrict__ logits) {
+    const uint16_t* __restrict__ P, const uint16_t* __restrict__ Z, int K, int64_t V, int k,
+    const T* __restrict__ W, const T* __restrict__ H, int d, int32_t* __restrict__ idx, float* __restrict__ score,
+    float* __restrict__ logits) {
   __shared__ MergeSmem m;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t b = blockIdx.y;
@@ -72,7 +73,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
 
   // 1-2. the leading entries of every list, the bound, the candidates
   const int64_t R = b * (int64_t)L * n;   // row base
-  const int nc = merge_collect(m, part_s + R, part_i + R, n, L, raw ? raw + b * V : nullptr, V, k);
+  const RowScores src{raw ? raw + b * V : nullptr, raw ? nullptr : P, raw || !P ? nullptr : Z + b * K, K};
+  const int nc = merge_collect(m, part_s + R, part_i + R, n, L, src, V, k);
 
   // 3. selection, with the rescoring in flight when it can be
   const bool fits = nc <= kCandSlots;
@@ -87,8 +89,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
       m.top_s[lane] = s;
       m.top_i[lane] = i;
     } else {
-      // ties flag too many candidates: the k best of the row's raw scores
-      select_raw_row(m, raw + b * V, V, k);
+      // ties flag too many candidates: the k best of all the row's scores
+      select_raw_row(m, src, V, k);
     }
   } else if (spec) {
     // this block's candidates in slot order; the t-th goes to wave 1 + t % 7
@@ -154,26 +156,28 @@ hipError_t launch_rescore(int dtype, const void* W, const void* H, const int32_t
 }
 
 hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, const float* raw,
-                        int64_t V, int64_t B, int k, const void* W, const void* H, int d, int32_t* idx,
-                        float* score, float* logits, hipStream_t stream) {
+                        const void* P, const void* Z, int K, int64_t V, int64_t B, int k, const void* W,
+                        const void* H, int d, int32_t* idx, float* score, float* logits, hipStream_t stream) {
   if (n < 1 || n > kMaxLists || L < 1 || L > k) return hipErrorInvalidValue;
-  if (L < k && !raw) return hipErrorInvalidValue;
+  if (L < k && !raw && !(P && Z && K >= 32 && K % 32 == 0)) return hipErrorInvalidValue;
+  const uint16_t* Pm = static_cast<const uint16_t*>(P);
+  const uint16_t* Zm = static_cast<const uint16_t*>(Z);
   const dim3 block(kMergeThreads);
   if (!logits) {
     const dim3 grid(1, (unsigned)B);
-    hipLaunchKernelGGL((merge_kernel<uint16_t, false>), grid, block, 0, stream, part_s, part_i, n, L, raw, V, k,
-                       (const uint16_t*)nullptr, (const uint16_t*)nullptr, d, idx, score, logits);
+    hipLaunchKernelGGL((merge_kernel<uint16_t, false>), grid, block, 0, stream, part_s, part_i, n, L, raw, Pm, Zm, K,
+                       V, k, (const uint16_t*)nullptr, (const uint16_t*)nullptr, d, idx, score, logits);
     return hipGetLastError();
   }
   // enough blocks that waves 1..7 of all of them can hold 2k candidates
   const int G = (2 * k + kMergeWaves - 2) / (kMergeWaves - 1);
   const dim3 grid((unsigned)G, (unsigned)B);
   if (dtype == 0)
-    hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, block, 0, stream, part_s, part_i, n, L, raw, V, k,
-                       (const uint16_t*)W, (const uint16_t*)H, d, idx, score, logits);
+    hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, block, 0, stream, part_s, part_i, n, L, raw, Pm, Zm, K,
+                       V, k, (const uint16_t*)W, (const uint16_t*)H, d, idx, score, logits);
   else
-    hipLaunchKernelGGL((merge_kernel<float, true>), grid, block, 0, stream, part_s, part_i, n, L, raw, V, k,
-                       (const float*)W, (const float*)H, d, idx, score, logits);
+    hipLaunchKernelGGL((merge_kernel<float, true>), grid, block, 0, stream, part_s, part_i, n, L, raw, Pm, Zm, K, V,
+                       k, (const float*)W, (const float*)H, d, idx, score, logits);
   return hipGetLastError();
 }
 

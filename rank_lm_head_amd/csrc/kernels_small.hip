@@ -124,6 +124,184 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
   }
 }
 
+// ------------------------------------------- score pass, 9 to 64 rows
+// The matrix-core stream (stream_mfma_tiles) with NB/16 column tiles of z,
+// and no score leaves the registers: each lane keeps, for each of its rows
+// of z (16 c + (l & 15) in column tile c), the 4 best of the vocabulary rows
+// it is handed (rows 4 (l >> 4) .. +3 of every 16-row tile of its wave's
+// quarter of the slice), in candidate order. At the end the block merges its
+// 16 lists per row of z (4 waves x 4 lane groups) through LDS and writes the
+// slice's L best, entry j to part_[b][j][x] (depth-major, as
+// select_short_kernel). No raw scores are kept: a slice that the merge needs
+// more of is recomputed there in the same arithmetic.
+
+// Inserts (x, id) into a list in candidate order whose empty slots hold NaN
+// (at the end). The ids a list is handed increase, so an entry with an equal
+// score precedes x: x goes below every entry it does not beat, or into the
+// first empty slot (!(s >= x) holds for both). c[e] (x goes at e or above)
+// implies c[e + 1], so every slot takes one of three values. Branch-free.
+__device__ __forceinline__ void list_insert4(float (&ts)[kSliceList], int (&ti)[kSliceList], float x, int id) {
+  static_assert(kSliceList == 4, "four entries");
+  bool c[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c[e] = !(ts[e] >= x);
+#pragma unroll
+  for (int e = 3; e > 0; --e) {
+    const float s1 = c[e] ? x : ts[e];
+    const int i1 = c[e] ? id : ti[e];
+    ts[e] = c[e - 1] ? ts[e - 1] : s1;
+    ti[e] = c[e - 1] ? ti[e - 1] : i1;
+  }
+  ts[0] = c[0] ? x : ts[0];
+  ti[0] = c[0] ? id : ti[0];
+}
+
+// a := the 4 best of lists a and b (each in candidate order, empty entries
+// (-inf, kSentinelId) last), in order: the better of a[i] and b[3 - i] for
+// each i are the 4 best, as a bitonic sequence, which two rounds of
+// compare-exchanges put in order.
+__device__ __forceinline__ void merge_list4(float (&as)[4], int (&ai)[4], const float (&bs)[4], const int (&bi)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool keep = precedes(as[i], ai[i], bs[3 - i], bi[3 - i]);
+    as[i] = keep ? as[i] : bs[3 - i];
+    ai[i] = keep ? ai[i] : bi[3 - i];
+  }
+  auto cx = [&](int x, int y) {
+    const bool keep = precedes(as[x], ai[x], as[y], ai[y]);
+    const float sx = as[x], sy = as[y];
+    const int ix = ai[x], iy = ai[y];
+    as[x] = keep ? sx : sy;
+    ai[x] = keep ? ix : iy;
+    as[y] = keep ? sy : sx;
+    ai[y] = keep ? iy : ix;
+  };
+  cx(0, 2);
+  cx(1, 3);
+  cx(0, 1);
+  cx(2, 3);
+}
+
+// The lists of a block in LDS, the row of z innermost: the 16 lanes of a
+// lane group write (and the threads of the merge read) consecutive words,
+// and the rows of one lane group are padded by 4 words, so that the four
+// lane groups of a wave fall on different banks.
+template <int NB>
+struct RowsLds {
+  static constexpr int kRow = NB + 4;
+  float ls[kWavesSmall][4][kSliceList][kRow];         // wave, lane group, entry, row of z
+  int li[kWavesSmall][4][kSliceList][kRow];
+};
+
+template <int K, int NB>
+__global__ void __launch_bounds__(kSmallThreads) select_rows_kernel(
+    const uint16_t* __restrict__ M, const uint16_t* __restrict__ X, int64_t V, int B, int L,
+    float* __restrict__ part_s, int* __restrict__ part_i) {
+  static_assert(NB == 16 || NB == 32 || NB == 64, "column tiles of 16 rows");
+  constexpr int NT = NB / 16;
+  constexpr int KS = K / 32;
+  constexpr int TG = KS >= 4 ? 1 : 4 / KS;   // about 4 wave loads per group (more measured slower)
+  __shared__ RowsLds<NB> sm;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+
+  // slice bounds V*x/n in 32 bits: this path keeps V*n below 2^32
+  const int64_t nblk = gridDim.x;
+  const uint32_t v32 = (uint32_t)V, n32 = gridDim.x;
+  const int64_t blo = v32 * blockIdx.x / n32, bhi = v32 * (blockIdx.x + 1) / n32;
+  const int64_t wlo = blo + (bhi - blo) * wave / kWavesSmall;
+  const int64_t whi = blo + (bhi - blo) * (wave + 1) / kWavesSmall;
+
+  float ts[NT][kSliceList];
+  int ti[NT][kSliceList];
+#pragma unroll
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int e = 0; e < kSliceList; ++e) {
+      ts[c][e] = __builtin_nanf("");
+      ti[c][e] = kSentinelId;
+    }
+  // ids in 32 bits (V < 2^31); a tile past the wave's range (its last one)
+  // keeps only its rows below whi
+  const int whi32 = (int)whi;
+  // (the column tiles' lists are independent: interleaved for the scheduler)
+  stream_mfma_tiles<K, NT, TG>(M, X, B, wlo, whi, [&](int64_t base, const f32x4 (&acc)[NT]) {
+    const int row0 = (int)base + 4 * g;
+    if ((int)base + 16 <= whi32) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int c = 0; c < NT; ++c) list_insert4(ts[c], ti[c], acc[c][q], row0 + q);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (row0 + q < whi32) {
+#pragma unroll
+          for (int c = 0; c < NT; ++c) list_insert4(ts[c], ti[c], acc[c][q], row0 + q);
+        }
+    }
+  });
+
+  // the 16 lists of each row of z (4 waves x 4 lane groups) to LDS; then T
+  // consecutive lanes per row of z (T = 256 / NB: 4, 8 or 16, inside one
+  // wave) each merge 16 / T of them, and a butterfly over the T lanes (DPP
+  // exchanges; both partners compute the same merge, as the order is total)
+  // leaves the row's 4 best on all of them
+#pragma unroll
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int e = 0; e < kSliceList; ++e) {
+      const bool empty = ti[c][e] == kSentinelId;
+      sm.ls[wave][g][e][c * 16 + col] = empty ? neg_inf() : ts[c][e];
+      sm.li[wave][g][e][c * 16 + col] = ti[c][e];
+    }
+  __syncthreads();
+  constexpr int T = kSmallThreads / NB, PER = kWavesSmall * 4 / T;
+  const int b = threadIdx.x / T, p = threadIdx.x % T;
+  float as[4], bs[4];
+  int ai[4], bi[4];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int list = p * PER + j, w = list >> 2, gg = list & 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bs[e] = sm.ls[w][gg][e][b];
+      bi[e] = sm.li[w][gg][e][b];
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        as[e] = bs[e];
+        ai[e] = bi[e];
+      }
+    } else {
+      merge_list4(as, ai, bs, bi);
+    }
+  }
+  auto exchange = [&](auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bs[e] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(as[e]), C, 0xf, 0xf, true));
+      bi[e] = __builtin_amdgcn_mov_dpp(ai[e], C, 0xf, 0xf, true);
+    }
+    merge_list4(as, ai, bs, bi);
+  };
+  exchange(std::integral_constant<int, 0xB1>{});                           // lane ^ 1
+  exchange(std::integral_constant<int, 0x4E>{});                           // lane ^ 2
+  if constexpr (T >= 8) exchange(std::integral_constant<int, 0x141>{});    // 7 - lane in 8
+  if constexpr (T >= 16) exchange(std::integral_constant<int, 0x128>{});   // lane + 8 in 16
+  if (p == 0 && b < B) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < L) {
+        const int64_t o = ((int64_t)b * L + e) * nblk + blockIdx.x;
+        part_s[o] = as[e];
+        part_i[o] = ai[e];
+      }
+  }
+}
+
 // -------------------------------------------- score pass, long rows (W . h)
 // One vocabulary row at a time per wave: NL wave loads of 1 KiB (K <= NL *
 // 512), the next row's loads issued before the current row is reduced. The
@@ -260,6 +438,51 @@ static int row_loads(int K) {
   } while (0)
 
 int small_list_len(int k) { return k < kSliceList ? k : kSliceList; }
+
+// 9 to 64 rows: column tiles of 16, 32 or 64 rows of z; the fragments of z
+// held in registers (NB/16 x K/32 of 16 bytes a lane) stay at 64 VGPRs.
+bool rows_path(int dtype, int64_t B, int64_t K_lowrank, int64_t V) {
+  if (dtype != 0 || B <= kSmallB || B > kRowsMaxB) return false;
+  if (V > (int64_t)kMaxSmallBlocks * kBlockRows) return false;
+  if (K_lowrank < 32 || K_lowrank > 512 || (K_lowrank & (K_lowrank - 1)) != 0) return false;
+  const int64_t nb = B <= 16 ? 16 : B <= 32 ? 32 : 64;
+  return nb * K_lowrank <= 16 * 512;
+}
+
+template <int K>
+static hipError_t launch_rows_k(const void* M, const void* X, int64_t V, int64_t B, int k, float* ps, int* pi,
+                                hipStream_t stream, Timing t) {
+  const int nblk = small_blocks(V);
+  const int L = small_list_len(k);
+  if (!rows_path(0, B, K, V) || V * nblk >= (int64_t)1 << 32) return hipErrorInvalidValue;
+  const dim3 grid(nblk), block(kSmallThreads);
+#define LRH_RW(NB)                                                                                        \
+  LRH_LAUNCH(t, (select_rows_kernel<K, NB>), grid, block, 0, stream, (const uint16_t*)M, (const uint16_t*)X, V, \
+             (int)B, L, ps, pi)
+  if (B <= 16) {
+    LRH_RW(16);
+  } else if constexpr (K <= 256) {
+    if (B <= 32) {
+      LRH_RW(32);
+    } else if constexpr (K <= 128) {
+      LRH_RW(64);
+    }
+  }
+#undef LRH_RW
+  return hipGetLastError();
+}
+
+hipError_t launch_select_rows(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* ps,
+                              int* pi, hipStream_t stream, Timing t) {
+  switch (K) {
+    case 32: return launch_rows_k<32>(M, X, V, B, k, ps, pi, stream, t);
+    case 64: return launch_rows_k<64>(M, X, V, B, k, ps, pi, stream, t);
+    case 128: return launch_rows_k<128>(M, X, V, B, k, ps, pi, stream, t);
+    case 256: return launch_rows_k<256>(M, X, V, B, k, ps, pi, stream, t);
+    case 512: return launch_rows_k<512>(M, X, V, B, k, ps, pi, stream, t);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 template <int K>
 static hipError_t launch_short_k(const void* M, const void* X, int64_t V, int64_t B, int k, float* ps, int* pi,

@@ -47,6 +47,14 @@ hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, i
                                int* part_i, float* raw, hipStream_t stream, Timing t = {});
 hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
                               int* part_i, hipStream_t stream, Timing t = {});
+// 9 to kRowsMaxB draft rows (bf16, power-of-two r >= 32, at most 8192
+// elements of z in a column tile group): the same slice lists from the
+// matrix-core stream, no raw scores (the merge recomputes a slice it needs
+// more of).
+constexpr int kRowsMaxB = 64;
+bool rows_path(int dtype, int64_t B, int64_t K, int64_t V);
+hipError_t launch_select_rows(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
+                              int* part_i, hipStream_t stream, Timing t = {});
 
 // ------------------------------------------------------- kernels_b1.hip
 // z = round(Q . h) for B <= kDownWideMaxB rows, one block per row of Q and
@@ -151,12 +159,14 @@ hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, i
 // Merges n sorted lists of L entries per row (part_[row][entry][list],
 // n <= 512) into the k best, to idx / score (score may be NULL). Lists
 // shorter than k (L < k) come with the rows' raw scores (raw[row][v], list p
-// holding the best of the slice [V*p/n, V*(p+1)/n)); with L == k, raw may be
-// NULL. With logits != NULL, also writes the winners' exact logits
-// W[id] . h_b.
+// holding the best of the slice [V*p/n, V*(p+1)/n)), or, with raw NULL, with
+// P (V x K) and Z (B x K), bf16, from which the merge recomputes the scores
+// of a slice it needs (lists from the matrix-core stream only); with L == k
+// all three may be NULL. With logits != NULL, also writes the winners'
+// exact logits W[id] . h_b.
 hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, const float* raw,
-                        int64_t V, int64_t B, int k, const void* W, const void* H, int d, int32_t* idx,
-                        float* score, float* logits, hipStream_t stream);
+                        const void* P, const void* Z, int K, int64_t V, int64_t B, int k, const void* W,
+                        const void* H, int d, int32_t* idx, float* score, float* logits, hipStream_t stream);
 
 // ---------------------------------------------------- kernels_branch.hip
 // Softmax of each row's k candidate logits, the nb most probable as

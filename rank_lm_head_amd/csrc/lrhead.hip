@@ -47,6 +47,12 @@ namespace {
 constexpr uint32_t kMagic = 0x4c524844u;  // "LRHD"
 constexpr int64_t kDownGemmRows = 256;     // rows from which z = Q . h may run on the GEMM kernel
 constexpr int64_t kDownSplitMaxElems = 65536;   // ... when B * r is above this
+// From this many rows on, the 9-64 row path ranks in the merge and rescores
+// the winners in a launch of their own: the merge's speculative rescoring of
+// every candidate (a few more than k per row) reads more of W than it hides
+// (cold calls at r = 128, k = 32: 31.2 against 30.1 us at 32 rows, 44.2
+// against 39.7 at 64; 27.3 against 29.1 at 24).
+constexpr int64_t kRowsRescoreApart = 32;
 constexpr int64_t kBMaxLimit = int64_t(1) << 20;
 
 thread_local char g_err[512] = "";
@@ -77,7 +83,7 @@ int64_t max_list_rows(int64_t B_max, int64_t V) {
   int64_t best = 0;
   for (int64_t B = 1; B <= B_max; ++B) {
     int64_t rows = B * lrh::plan_vsplit(B, V);
-    if (B <= lrh::kSmallB) {
+    if (B <= lrh::kRowsMaxB) {
       const int64_t small = B * lrh::small_blocks(V);
       if (small > rows) rows = small;
     }
@@ -186,7 +192,8 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
     LRH_HIP(lrh::launch_draft1(a, s, timing(h)), "score/selection launch");
     return LRHEAD_OK;
   }
-  const bool streaming = lrh::small_path(h->dtype, B, h->r, h->V);
+  const bool rows = lrh::rows_path(h->dtype, B, h->r, h->V);
+  const bool streaming = rows || lrh::small_path(h->dtype, B, h->r, h->V);
   if (!streaming && lrh::batch_path(h->dtype, B)) {
     // many rows. Up to 64 rows the down-projection takes one block per row
     // of Q and group of 8 rows (one launch); above that it is a GEMM worth
@@ -217,12 +224,18 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   if (streaming) {
     LRH_HIP(lrh::launch_down_wide(h->Q, H, (int)h->r, (int)h->d, B, h->z, nullptr, 0, nullptr, 0, s),
             "down-projection launch");
-    LRH_HIP(lrh::launch_select_small(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, h->raw, s,
-                                     timing(h)),
-            "score/selection launch");
+    if (rows) {
+      // no raw scores: the merge recomputes a slice it needs more of
+      LRH_HIP(lrh::launch_select_rows(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, s, timing(h)),
+              "score/selection launch");
+    } else {
+      LRH_HIP(lrh::launch_select_small(h->P, h->z, h->V, (int)h->r, B, k, h->part_s, h->part_i, h->raw, s,
+                                       timing(h)),
+              "score/selection launch");
+      raw = h->raw;
+    }
     n_lists = lrh::small_blocks(h->V);
     list_len = lrh::small_list_len(k);
-    raw = h->raw;
   } else {
     LRH_HIP(lrh::launch_down(h->dtype, h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
     n_lists = lrh::plan_vsplit(B, h->V);
@@ -230,8 +243,18 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
                                timing(h)),
             "score/selection launch");
   }
-  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, raw, h->V, B, k, h->W, H,
-                            (int)h->d, idx, score, logits, s),
+  if (rows && B >= kRowsRescoreApart) {
+    // the merge ranks only; the winners' logits come from their own launch
+    LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, raw, h->P, h->z, (int)h->r, h->V, B,
+                              k, nullptr, nullptr, (int)h->d, idx, score, nullptr, s),
+            "merge launch");
+    if (logits)
+      LRH_HIP(lrh::launch_rescore(h->dtype, h->W, H, idx, B, k, h->V, (int)h->d, logits, s), "rescore launch");
+    return LRHEAD_OK;
+  }
+  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, raw, rows ? h->P : nullptr,
+                            rows ? h->z : nullptr, (int)h->r, h->V, B, k, h->W, H, (int)h->d, idx, score, logits,
+                            s),
           "merge launch");
   return LRHEAD_OK;
 }
@@ -398,8 +421,8 @@ int fullhead_topk(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, flo
                                timing(h)),
             "full-head selection launch");
   }
-  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, k, nullptr, h->V, B, k, nullptr, nullptr,
-                            (int)h->d, idx, logits, nullptr, s),
+  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, k, nullptr, nullptr, nullptr, 0, h->V, B, k,
+                            nullptr, nullptr, (int)h->d, idx, logits, nullptr, s),
           "merge launch");
   return LRHEAD_OK;
 }

@@ -10,10 +10,11 @@
 //                    histogram of score images) and gathers the entries that
 //                    reach it (a few more than k) as candidate keys; lists
 //                    whose last leading entry still reaches T are read further
-//                    (their list, or their slice's raw scores).
+//                    (their list, or their slice's scores: raw, or recomputed).
 //  select_candidates ranks the candidates (wave 0).
 //  select_raw_row    the fallback when ties flag more candidates than the
-//                    buffer holds: the k best of the row's raw scores.
+//                    buffer holds: the k best of the row's raw (or
+//                    recomputed) scores.
 //
 // The order is the head's candidate order: higher score first, the lower id
 // on equal scores ("EAGLE-4", section "Retrieve vocabulary candidates
@@ -120,11 +121,62 @@ __device__ __forceinline__ void push_cands(MergeSmem& m, bool ps, uint64_t key) 
   }
 }
 
+// The scores of a row beyond its slice lists: the row's raw scores (raw),
+// or, with raw == NULL and P != NULL, recomputed from P (V x K, bf16) and
+// the row's z (K entries, bf16) on the matrix cores in the arithmetic of the
+// score pass that made the lists (stream_mfma_tiles: per 16-row tile one
+// v_mfma_f32_16x16x32_bf16 per 32 of K, accumulated in order from zero), so
+// that a recomputed score equals the listed one bit for bit.
+struct RowScores {
+  const float* raw;
+  const uint16_t* P;
+  const uint16_t* z;
+  int K;
+};
+
+// The row (0..63) whose recomputed score lane l holds after recompute64:
+// column l & 15 of every output tile carries the same z, so lane l keeps
+// output (l & 15) & 3 of tile (l & 15) >> 2, i.e. tile row 4 (l >> 4) + q.
+__device__ __forceinline__ int recompute_row(int lane) {
+  const int g = lane >> 4, col = lane & 15;
+  return 16 * (col >> 2) + 4 * g + (col & 3);
+}
+
+// One wave: the scores of rows c0 + recompute_row(lane) (rows at or past hi
+// are computed on row hi - 1 and are the caller's to drop).
+__device__ __forceinline__ float recompute64(const RowScores& src, int64_t c0, int64_t hi) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+  f32x4 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ks = src.K / 32;
+  for (int t = 0; t < ks; ++t) {
+    const u32x4 zb = load16(src.z + t * 32 + g * 8);
+    u32x4 a[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t row = min(c0 + 16 * c + col, hi - 1);
+      a[c] = load16(src.P + row * src.K + t * 32 + g * 8);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[c]),
+                                                       __builtin_bit_cast(bf16x8, zb), acc[c], 0, 0, 0);
+  }
+  float x = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x = (col >> 2) == c && (col & 3) == q ? acc[c][q] : x;
+  return x;
+}
+
 // Steps 1-2 of the merge of row b, by all 512 threads: list p (p < n <= 512)
 // is read by thread p; entry j of list p sits at lists_s/i[j * n + p] (the
-// row's depth-major block). raw (may be NULL when L >= k) holds the row's raw
-// scores, slice p being [V*p/n, V*(p+1)/n). Returns the candidate count
-// (past kCandSlots: the buffer overflowed and only the count is right).
+// row's depth-major block). src (raw and P both NULL when L >= k) gives the
+// row's scores, slice p being [V*p/n, V*(p+1)/n). Returns the candidate
+// count (past kCandSlots: the buffer overflowed and only the count is right).
 //
 // Take any bound T that at least k list entries reach. Then an entry below
 // T is preceded by k others and cannot win, and a list whose head is below T
@@ -134,7 +186,8 @@ __device__ __forceinline__ void push_cands(MergeSmem& m, bool ps, uint64_t key) 
 // images, so at least k entries reach T. With k heads or fewer, T = 1 and
 // every non-empty entry counts.
 __device__ __forceinline__ int merge_collect(MergeSmem& m, const float* __restrict__ lists_s,
-                                             const int* __restrict__ lists_i, int n, int L, const float* __restrict__ raw, int64_t V, int k) {
+                                             const int* __restrict__ lists_i, int n, int L, const RowScores& src,
+                                             int64_t V, int k) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int F = min(kFront, L);
   const int p = threadIdx.x;
@@ -229,8 +282,8 @@ __device__ __forceinline__ int merge_collect(MergeSmem& m, const float* __restri
       }
     }
     // a slice whose last front entry reaches the bound may hold more: the
-    // rest of its list (L > F), or its raw scores (lists shorter than k)
-    const bool more = L > F || (L < k && raw != nullptr);
+    // rest of its list (L > F), or its scores (lists shorter than k)
+    const bool more = L > F || (L < k && (src.raw != nullptr || src.P != nullptr));
     if (more && (pass >> (F - 1)) & 1u) {
       const int dl = atomicAdd(&m.n_deep, 1);
       m.deep[dl] = p;
@@ -252,18 +305,27 @@ __device__ __forceinline__ int merge_collect(MergeSmem& m, const float* __restri
           push_cands(m, reaches(sc, id), cand_key(sc, id));
         }
       } else {
-        // the slice's raw scores below its list's last entry that reach T
+        // the slice's scores below its list's last entry that reach T
         const int64_t lo = V * q / n, hi = V * (q + 1) / n;
         const uint64_t below = m.deep_key[dl];
-        for (int64_t c0 = lo; c0 < hi; c0 += 8 * kWave) {
-          float xs[8];
+        if (src.raw) {
+          for (int64_t c0 = lo; c0 < hi; c0 += 8 * kWave) {
+            float xs[8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) xs[t] = raw[min(c0 + t * kWave + lane, hi - 1)];
+            for (int t = 0; t < 8; ++t) xs[t] = src.raw[min(c0 + t * kWave + lane, hi - 1)];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int64_t v = c0 + t * kWave + lane;
-            const uint64_t key = v < hi ? cand_key(xs[t], (int)v) : 0ull;
-            push_cands(m, key != 0 && key < below && reaches(xs[t], (int)v), key);
+            for (int t = 0; t < 8; ++t) {
+              const int64_t v = c0 + t * kWave + lane;
+              const uint64_t key = v < hi ? cand_key(xs[t], (int)v) : 0ull;
+              push_cands(m, key != 0 && key < below && reaches(xs[t], (int)v), key);
+            }
+          }
+        } else {
+          for (int64_t c0 = lo; c0 < hi; c0 += kWave) {
+            const float x = recompute64(src, c0, hi);
+            const int64_t v = c0 + recompute_row(lane);
+            const uint64_t key = v < hi ? cand_key(x, (int)v) : 0ull;
+            push_cands(m, key != 0 && key < below && reaches(x, (int)v), key);
           }
         }
       }
@@ -344,9 +406,35 @@ __device__ __forceinline__ void select_keys_seq(int64_t count, int k, KeyAt key_
 }
 
 // Wave 0, when ties flag more candidates than the buffer holds: the k best
-// of the row's V raw scores.
-__device__ __forceinline__ void select_raw_row(MergeSmem& m, const float* __restrict__ raw, int64_t V, int k) {
-  select_keys_seq(V, k, [&](int64_t v) { return cand_key(raw[v], (int)v); }, m.top_s, m.top_i, m.tmp);
+// of the row's V scores, raw or recomputed (64 rows per recompute64, the
+// rows of a chunk in recompute_row order).
+__device__ __forceinline__ void select_raw_row(MergeSmem& m, const RowScores& src, int64_t V, int k) {
+  if (src.raw) {
+    const float* raw = src.raw;
+    select_keys_seq(V, k, [&](int64_t v) { return cand_key(raw[v], (int)v); }, m.top_s, m.top_i, m.tmp);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  m.top_s[lane] = neg_inf();
+  m.top_i[lane] = kSentinelId;
+  const int64_t perm = recompute_row(lane);
+  for (int64_t c0 = 0; c0 < V; c0 += 7 * kWave) {
+    uint64_t key[8];
+#pragma unroll
+    for (int e = 0; e < 7; ++e) {
+      const int64_t r0 = c0 + e * kWave;
+      key[e] = 0ull;
+      if (r0 < V) {
+        const float x = recompute64(src, r0, V);
+        if (r0 + perm < V) key[e] = cand_key(x, (int)(r0 + perm));
+      }
+    }
+    key[7] = lane < k && m.top_i[lane] != kSentinelId ? cand_key(m.top_s[lane], m.top_i[lane]) : 0ull;
+    wave_topk_emit<8>(key, k, m.tmp, m.top_s, m.top_i);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 }
 
 }  // namespace lrh

@@ -83,28 +83,35 @@ __device__ __forceinline__ void stream_scores(const uint16_t* __restrict__ M, co
   }
 }
 
-// The same scores on the matrix cores, for 2 to 8 rows (K >= 32): one
-// v_mfma_f32_16x16x32_bf16 multiplies 16 rows of M by the rows of X (padded
-// to 16 with zeros) over 32 of K, so the vector ALU no longer widens and
-// multiplies every element once per row. Lane l supplies row l & 15 of the
-// 16-row tile and chunk l >> 4 (8 elements) of each 32-deep step; output q
-// of lane l is the score of tile row 4 (l >> 4) + q for row l & 15 of X.
-// X's fragments stay in registers for the whole pass. The wave's rows go in
-// tiles of 16, two groups of about 8 wave loads in flight (non-temporal);
-// rows past the wave's range are loaded from its last row and never kept.
-template <int K, int NB>
-__device__ __forceinline__ void stream_scores_mfma(const uint16_t* __restrict__ M, const uint16_t* __restrict__ X,
-                                                   int B, int64_t blo, int64_t wlo, int64_t whi, float* sc,
-                                                   int ldsc) {
-  static_assert(K % 32 == 0 && NB <= 16, "k steps of 32, at most 16 rows of X");
-  constexpr int KS = K / 32;                         // k steps per tile
-  constexpr int TG = KS >= 8 ? 1 : 8 / KS;           // tiles per group
+// The matrix-core tile stream over rows [wlo, whi) of M (V x K, bf16)
+// against NT column tiles of X (16 rows each; rows past B are zeros). One
+// v_mfma_f32_16x16x32_bf16 multiplies 16 rows of M by 16 rows of X over 32
+// of K, so the vector ALU no longer widens and multiplies every element once
+// per row. Lane l supplies row l & 15 of the 16-row tile and chunk l >> 4 (8
+// elements) of each 32-deep step, the k steps accumulate in order from
+// zero. For every 16-row tile the stream calls sink(base, acc) (base: the
+// tile's first row, the same on all lanes): acc[c][q] is the score of M row
+// base + 4 (l >> 4) + q against X row 16 c + (l & 15) (column tile c); rows
+// at or past whi are the sink's to drop. X's fragments stay in registers for the whole pass.
+// The tiles go in groups of TG, two groups of loads in flight
+// (non-temporal); rows past the wave's range are loaded from its last row (a
+// valid address, so no load is predicated), and the last group prefetches
+// nothing, so no load is outstanding when the function returns.
+template <int K, int NT, int TG, typename Sink>
+__device__ __forceinline__ void stream_mfma_tiles(const uint16_t* __restrict__ M, const uint16_t* __restrict__ X,
+                                                  int B, int64_t wlo, int64_t whi, Sink&& sink) {
+  static_assert(K % 32 == 0 && NT >= 1 && NT <= 4, "k steps of 32, at most 64 rows of X");
+  constexpr int KS = K / 32;   // k steps per tile
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, col = lane & 15;
-  u32x4 xb[KS];
+  u32x4 xb[NT][KS];
 #pragma unroll
-  for (int t = 0; t < KS; ++t)
-    xb[t] = col < B && col < NB ? load16(X + (int64_t)col * K + t * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const int b = c * 16 + col;
+      xb[c][t] = b < B ? load16(X + (int64_t)b * K + t * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
   const int64_t last = whi > 0 ? whi - 1 : 0;
   const int ng = wlo < whi ? (int)((whi - wlo + 16 * TG - 1) / (16 * TG)) : 0;
   u32x4 buf0[TG][KS], buf1[TG][KS];
@@ -120,18 +127,16 @@ __device__ __forceinline__ void stream_scores_mfma(const uint16_t* __restrict__ 
   auto consume = [&](const u32x4 (&buf)[TG][KS], int64_t base) {
 #pragma unroll
     for (int u = 0; u < TG; ++u) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[NT];
 #pragma unroll
-      for (int t = 0; t < KS; ++t)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[u][t]),
-                                                      __builtin_bit_cast(bf16x8, xb[t]), acc, 0, 0, 0);
-      if (col < B && col < NB) {
+      for (int c = 0; c < NT; ++c) {
+        acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t row = base + u * 16 + 4 * g + q;
-          if (row < whi) sc[col * ldsc + (row - blo)] = acc[q];
-        }
+        for (int t = 0; t < KS; ++t)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[u][t]),
+                                                           __builtin_bit_cast(bf16x8, xb[c][t]), acc[c], 0, 0, 0);
       }
+      sink(base + u * 16, acc);
     }
   };
   issue(buf0, wlo);
@@ -151,6 +156,29 @@ __device__ __forceinline__ void stream_scores_mfma(const uint16_t* __restrict__ 
   } else if (gi < ng) {
     consume(buf0, wlo + (int64_t)gi * 16 * TG);
   }
+}
+
+// The scores of stream_scores on the matrix cores, for 2 to 16 rows (K >=
+// 32): one column tile of X, groups of about 8 wave loads, every score of a
+// row of X below B to sc[b * ldsc + (v - blo)].
+template <int K, int NB>
+__device__ __forceinline__ void stream_scores_mfma(const uint16_t* __restrict__ M, const uint16_t* __restrict__ X,
+                                                   int B, int64_t blo, int64_t wlo, int64_t whi, float* sc,
+                                                   int ldsc) {
+  static_assert(NB <= 16, "one column tile");
+  constexpr int KS = K / 32;
+  constexpr int TG = KS >= 8 ? 1 : 8 / KS;   // tiles per group
+  const int col = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
+  const int BB = B < NB ? B : NB;
+  stream_mfma_tiles<K, 1, TG>(M, X, BB, wlo, whi, [&](int64_t base, const f32x4 (&acc)[1]) {
+    if (col < BB) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t row = base + 4 * g + q;
+        if (row < whi) sc[col * ldsc + (row - blo)] = acc[0][q];
+      }
+    }
+  });
 }
 
 }  // namespace lrh

@@ -153,6 +153,56 @@ def test_batch_path_shapes(V, d, r, B, k):
     say(f"[ok] {stats}")
 
 
+@pytest.mark.parametrize("V,d,r,B,k", [
+    (257, 64, 32, 9, 9),         # two slices of 128 and 129 rows, 16-row column tile with 7 idle rows
+    (1000, 136, 32, 12, 5),      # ragged last 16-row tile of every wave
+    (300, 1032, 32, 20, 3),      # k < 4: lists of 3
+    (12345, 200, 64, 33, 10),    # 64-row column tiles at r = 64, 31 idle rows
+    (20000, 512, 256, 32, 40),   # 32-row column tiles at r = 256
+    (30000, 512, 512, 16, 64),   # r = 512 on one column tile
+    (6000, 384, 128, 64, 64),    # 64 rows at r = 128, k = 64
+    (200000, 64, 32, 40, 16),    # 391 rows per slice
+])
+def test_rows_path_shapes(V, d, r, B, k):
+    """9 to 64 rows: the matrix-core pass that keeps each slice's best in
+    registers, then the merge."""
+    inp = gen.make_custom(V, d, r, B, "bf16", seed=V + 3 * B)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=k)
+    say(f"[run] rows V={V} d={d} r={r} B={B} k={k}")
+    idx, score, lg = head.draft(t["H"], k)
+    torch.cuda.synchronize()
+    errs, stats = check_lowrank(inp, k, np_(idx), np_(score), np_(lg))
+    assert not errs, errs[:5]
+    say(f"[ok] {stats}")
+
+
+@pytest.mark.parametrize("B", [16, 64])
+def test_rows_path_best_inside_one_slice(B):
+    """P's rows in one slice scaled by 8 (exact in bf16), so that most of
+    every row's k best sit in that slice: its 4-entry lists are full at the
+    merge's bound and the merge recomputes the slice's scores, which must
+    equal the listed ones bit for bit for the result to be right."""
+    V, d, r, k = 20000, 256, 64, 32
+    inp = gen.make_custom(V, d, r, B, "bf16", seed=77 + B)
+    inp2 = dict(inp)
+    inp2["P"] = inp["P"].copy()
+    n = 79                                   # slices of this vocabulary (256 rows per block or fewer)
+    lo, hi = V * 3 // n, V * 4 // n
+    f = (inp["P"][lo:hi].astype(np.uint32) << np.uint32(16)).view(np.float32) * np.float32(8)
+    inp2["P"][lo:hi] = (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    t = {x: dev(inp2[x], DEV) for x in ("Q", "P", "W", "H")}
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=k)
+    say(f"[run] rows best inside one slice B={B}")
+    idx, score, lg = head.draft(t["H"], k)
+    torch.cuda.synchronize()
+    ids = np_(idx)
+    inside = ((ids >= lo) & (ids < hi)).sum(axis=1)
+    assert np.all(inside >= 5), inside
+    errs, _ = check_lowrank(inp2, k, ids, np_(score), np_(lg))
+    assert not errs, errs[:5]
+
+
 def test_batch_duplicate_rows_tie_to_the_lower_id():
     """Bitwise-equal vocabulary rows in different vocabulary blocks: the
     batch path returns them in id order (8 draft rows)."""
@@ -173,7 +223,7 @@ def test_batch_duplicate_rows_tie_to_the_lower_id():
     assert len(set(np_(score)[0].tolist())) == 1
 
 
-@pytest.mark.parametrize("B", [1, 8])
+@pytest.mark.parametrize("B", [1, 8, 16, 64])
 def test_all_scores_tied(B):
     """Every score equal: the k lowest ids win, in order (forces the merge's
     exhaustive path, since every entry reaches the sampled threshold)."""
@@ -351,7 +401,7 @@ def test_duplicate_rows_tie_to_the_lower_id():
     assert len(set(np_(flog)[0].tolist())) == 1
 
 
-@pytest.mark.parametrize("B", [1, 4, 8])
+@pytest.mark.parametrize("B", [1, 4, 8, 16, 40])
 def test_ties_inside_one_slice_go_to_the_lower_ids(B):
     """Bitwise copies of the best low-rank row inside one vocabulary slice, at
     ids that share a lane and ids in different lanes: every tied copy must come
@@ -387,7 +437,9 @@ def test_ties_inside_one_slice_go_to_the_lower_ids(B):
     (20000, 512, 128, 8, "bf16", False),   # eight-row streaming path
     (20000, 512, 128, 8, "bf16", True),    # eight rows, boundary ties
     (4096, 256, 32, 1, "fp32", False),     # fp32 (matrix-core slice lists and merge)
-    (20000, 512, 128, 40, "bf16", False),  # staged GEMM passes, down-projection in 8-row groups
+    (20000, 512, 128, 40, "bf16", False),  # 9-64 row pass, down-projection in 8-row groups
+    (20000, 512, 128, 40, "bf16", True),   # 9-64 row pass, boundary ties: the merge recomputes slices
+    (20000, 512, 256, 40, "bf16", False),  # staged GEMM passes (40 rows at r = 256)
     (20000, 512, 128, 300, "bf16", False), # strip kernel (two batch tiles), split down-projection in the score scratch
 ])
 def test_repeat_calls_and_poisoned_workspace_are_bitwise_stable(V, d, r, B, dt, ties):
