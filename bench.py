@@ -638,7 +638,7 @@ def main() -> int:
     n_b1 = max(1, min((cfg.V + 63) // 64, N_CU, B1_MAX_BLOCKS))
     one_row = cfg.dtype == "bf16" and cfg.B == 1 and pow2_r and (cfg.V + n_b1 - 1) // n_b1 <= B1_MAX_ROWS_PER_BLOCK
     col_tile = 16 if cfg.B <= 16 else 32 if cfg.B <= 32 else 64
-    rows = (cfg.dtype == "bf16" and 8 < cfg.B <= 64 and cfg.r in (32, 64, 128, 256, 512)
+    rows = (cfg.dtype == "bf16" and 5 <= cfg.B <= 64 and cfg.r in (32, 64, 128, 256, 512)
             and col_tile * cfg.r <= 16 * 512 and cfg.V <= 512 * 512)
     batch = cfg.dtype == "bf16" and cfg.B > 4 and not small and not rows
     if batch and cfg.r <= 256 and cfg.B > 256:
@@ -649,10 +649,10 @@ def main() -> int:
         sel_kernel, what = "draft1_kernel", "score stream + per-slice top-k + merge + rescoring of the winners"
         sel_bytes += (U + 1) * cfg.d * s + cfg.k * 12
         sel_flops += 2.0 * cfg.k * cfg.d
-    elif small:
-        sel_kernel, what = "select_short_kernel", "score pass + per-slice top-k"
     elif rows:
         sel_kernel, what = "select_rows_kernel", "matrix-core score pass + per-slice best 4 kept in registers"
+    elif small:
+        sel_kernel, what = "select_short_kernel", "score pass + per-slice top-k"
     else:
         sel_kernel, what = "select_mfma_kernel", "score pass + per-slice top-k"
     peak_flops = MFMA_PEAK_TFLOPS[cfg.dtype] * 1e12

@@ -439,10 +439,10 @@ static int row_loads(int K) {
 
 int small_list_len(int k) { return k < kSliceList ? k : kSliceList; }
 
-// 9 to 64 rows: column tiles of 16, 32 or 64 rows of z; the fragments of z
+// 5 to 64 rows: column tiles of 16, 32 or 64 rows of z; the fragments of z
 // held in registers (NB/16 x K/32 of 16 bytes a lane) stay at 64 VGPRs.
 bool rows_path(int dtype, int64_t B, int64_t K_lowrank, int64_t V) {
-  if (dtype != 0 || B <= kSmallB || B > kRowsMaxB) return false;
+  if (dtype != 0 || B < kRowsMinB || B > kRowsMaxB) return false;
   if (V > (int64_t)kMaxSmallBlocks * kBlockRows) return false;
   if (K_lowrank < 32 || K_lowrank > 512 || (K_lowrank & (K_lowrank - 1)) != 0) return false;
   const int64_t nb = B <= 16 ? 16 : B <= 32 ? 32 : 64;

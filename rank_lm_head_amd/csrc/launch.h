@@ -24,10 +24,13 @@ struct Timing {
       hipLaunchKernelGGL(kernel, grid, block, shm, stream, __VA_ARGS__);                         \
   } while (0)
 
-// Draft calls with up to kSmallB rows, and full-head calls with up to kLongB
-// rows, use the streaming kernels of kernels_small.hip (one pass over P or
-// W; the draft scores of 2-8 rows on the matrix cores, the rest on the
-// vector ALU); larger bf16 batches use the tiled matrix-core kernels.
+// Draft calls with up to kRowsMaxB rows, and full-head calls with up to
+// kLongB rows, use the streaming kernels of kernels_small.hip (one pass over
+// P or W): draft calls of kRowsMinB to kRowsMaxB rows the matrix-core pass
+// that keeps the slice lists in registers, smaller ones (and ranks below 32)
+// the pass that stages the scores in LDS (2-4 rows on the matrix cores, one
+// row and the full head on the vector ALU); larger bf16 batches use the tiled
+// matrix-core kernels.
 constexpr int kSmallB = 8;
 constexpr int kLongB = 4;
 
@@ -47,10 +50,13 @@ hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, i
                                int* part_i, float* raw, hipStream_t stream, Timing t = {});
 hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
                               int* part_i, hipStream_t stream, Timing t = {});
-// 9 to kRowsMaxB draft rows (bf16, power-of-two r >= 32, at most 8192
-// elements of z in a column tile group): the same slice lists from the
+// kRowsMinB to kRowsMaxB draft rows (bf16, power-of-two r >= 32, at most
+// 8192 elements of z in a column tile group): the same slice lists from the
 // matrix-core stream, no raw scores (the merge recomputes a slice it needs
-// more of).
+// more of). From 5 rows on it is the faster pass (cold calls at r = 128,
+// k = 32: 22.9 against 24.7 us at 8 rows, 21.6 against 21.8 at 4, 20.5
+// against 20.0 at 2).
+constexpr int kRowsMinB = 5;
 constexpr int kRowsMaxB = 64;
 bool rows_path(int dtype, int64_t B, int64_t K, int64_t V);
 hipError_t launch_select_rows(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,

@@ -102,10 +102,10 @@ def test_small_heads(dt, V, d, r, B, k):
     (777, 64, 32, 1, 5),
     (300, 1032, 8, 2, 3),        # k < 4, r = 8, d not a multiple of 512
     (9000, 8200, 64, 1, 16),     # d beyond the long-row kernel: matrix-core full head
-    (5000, 256, 128, 5, 64),     # five rows: the eight-row kernels with three idle rows
-    (30000, 512, 256, 8, 40),    # eight rows, many blocks
+    (5000, 256, 128, 5, 64),     # five rows: the register-list pass, 11 idle rows in its column tile
+    (30000, 512, 256, 8, 40),    # eight rows, many blocks (register-list pass)
     (777, 64, 32, 6, 5),
-    (300, 1032, 8, 7, 3),        # seven rows, r = 8, d not a multiple of 512
+    (300, 1032, 8, 7, 3),        # seven rows, r = 8 (LDS-staged pass), d not a multiple of 512
     (9000, 8200, 64, 8, 16),     # eight rows with d beyond the streaming down-projection
     (30000, 5120, 512, 4, 64),   # four rows at the drafter head's d, r at its maximum
     (200000, 64, 32, 8, 16),     # 391 rows per slice: the deepest score buffer
@@ -164,7 +164,7 @@ def test_batch_path_shapes(V, d, r, B, k):
     (200000, 64, 32, 40, 16),    # 391 rows per slice
 ])
 def test_rows_path_shapes(V, d, r, B, k):
-    """9 to 64 rows: the matrix-core pass that keeps each slice's best in
+    """5 to 64 rows: the matrix-core pass that keeps each slice's best in
     registers, then the merge."""
     inp = gen.make_custom(V, d, r, B, "bf16", seed=V + 3 * B)
     t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
@@ -322,10 +322,11 @@ def test_config_full_head_baseline(cid):
 
 # ------------------------------------------------------ invariants on the GPU
 
-@pytest.mark.parametrize("B", [1, 8, 20])
+@pytest.mark.parametrize("B", [1, 4, 8, 20, 64])
 def test_h_times_two_doubles_everything_bitwise(B):
     """h -> 2h is exact in bf16: z, scores and logits double bit for bit and
-    the ids stay (one-row pass, eight-row streaming path, row batch)."""
+    the ids stay (one-row pass, LDS-staged and register-list streaming
+    passes, the latter with the merge's own and separate rescoring)."""
     inp = gen.make_custom(5000, 256, 64, B, "bf16", seed=4)
     t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
     head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=32)
@@ -335,7 +336,7 @@ def test_h_times_two_doubles_everything_bitwise(B):
     assert np.array_equal(2 * a[1], b[1]) and np.array_equal(2 * a[2], b[2])
 
 
-@pytest.mark.parametrize("B", [1, 8, 20])
+@pytest.mark.parametrize("B", [1, 4, 8, 20, 64])
 def test_draft_logits_equal_rescoring_bitwise(B):
     """The draft call's logits (speculative per-slice rescoring and the merge's
     own, on the few-row paths) are the bits fullhead_logits gives for the same
@@ -434,11 +435,13 @@ def test_ties_inside_one_slice_go_to_the_lower_ids(B):
 @pytest.mark.parametrize("V,d,r,B,dt,ties", [
     (20000, 512, 128, 1, "bf16", False),   # one-row pass
     (20000, 512, 128, 1, "bf16", True),    # one-row pass, boundary ties: the merge reads raw scores
-    (20000, 512, 128, 8, "bf16", False),   # eight-row streaming path
-    (20000, 512, 128, 8, "bf16", True),    # eight rows, boundary ties
+    (20000, 512, 128, 4, "bf16", False),   # four-row streaming path (scores staged in LDS, raw copy)
+    (20000, 512, 128, 4, "bf16", True),    # four rows, boundary ties: the merge reads raw scores
+    (20000, 512, 128, 8, "bf16", False),   # eight rows: the register-list pass
+    (20000, 512, 128, 8, "bf16", True),    # eight rows, boundary ties: the merge recomputes slices
     (4096, 256, 32, 1, "fp32", False),     # fp32 (matrix-core slice lists and merge)
-    (20000, 512, 128, 40, "bf16", False),  # 9-64 row pass, down-projection in 8-row groups
-    (20000, 512, 128, 40, "bf16", True),   # 9-64 row pass, boundary ties: the merge recomputes slices
+    (20000, 512, 128, 40, "bf16", False),  # register-list pass, down-projection in 8-row groups
+    (20000, 512, 128, 40, "bf16", True),   # register-list pass, boundary ties: the merge recomputes slices
     (20000, 512, 256, 40, "bf16", False),  # staged GEMM passes (40 rows at r = 256)
     (20000, 512, 128, 300, "bf16", False), # strip kernel (two batch tiles), split down-projection in the score scratch
 ])
