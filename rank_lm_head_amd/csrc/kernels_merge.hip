@@ -41,8 +41,9 @@ __global__ void __launch_bounds__(256) rescore_kernel(const T* __restrict__ W, c
 }
 
 // ---------------------------------------------------------------- merge
-// Grid (G, B), 512 threads: block (g, b) merges row b's n lists (sorted,
-// depth-major: entry j of list p at part + (b * k + j) * n + p) and, with
+// Grid (G, B), 512 threads: block (g, b) merges row b's n lists (sorted;
+// depth-major: entry j of list p at part + (b * L + j) * n + p, or with
+// `rowmajor`: at part + (b * n + p) * L + j) and, with
 // RESCORE, gives the winners their exact logits. All G blocks of a row
 // compute the same winners; block 0 writes idx and score.
 //  1. The first 4 entries of every list are read in one coalesced pass (one
@@ -62,8 +63,9 @@ __global__ void __launch_bounds__(256) rescore_kernel(const T* __restrict__ W, c
 //     candidates, wave w of block g rescores winner g*per + w instead.
 template <typename T, bool RESCORE>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
-    const float* __restrict__ part_s, const int* __restrict__ part_i, int n, int L, const float* __restrict__ raw,
-    const uint16_t* __restrict__ P, const uint16_t* __restrict__ Z, int K, int64_t V, int k,
+    const float* __restrict__ part_s, const int* __restrict__ part_i, int n, int L, int rowmajor,
+    const float* __restrict__ raw, const uint16_t* __restrict__ P, const uint16_t* __restrict__ Z, int K, int64_t V,
+    int k,
     const T* __restrict__ W, const T* __restrict__ H, int d, int32_t* __restrict__ idx, float* __restrict__ score,
     float* __restrict__ logits) {
   __shared__ MergeSmem m;
@@ -73,8 +75,9 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
 
   // 1-2. the leading entries of every list, the bound, the candidates
   const int64_t R = b * (int64_t)L * n;   // row base
+  const ListLayout lay = rowmajor ? ListLayout{1, L} : ListLayout{n, 1};
   const RowScores src{raw ? raw + b * V : nullptr, raw ? nullptr : P, raw || !P ? nullptr : Z + b * K, K};
-  const int nc = merge_collect(m, part_s + R, part_i + R, n, L, src, V, k);
+  const int nc = merge_collect(m, part_s + R, part_i + R, n, L, lay, src, V, k);
 
   // 3. selection, with the rescoring in flight when it can be
   const bool fits = nc <= kCandSlots;
@@ -85,7 +88,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
     } else if (L == k) {
       float s;
       int i;
-      merge_lists_seq(part_s + R, part_i + R, n, k, s, i);
+      merge_lists_seq(part_s + R, part_i + R, n, k, lay, s, i);
       m.top_s[lane] = s;
       m.top_i[lane] = i;
     } else {
@@ -155,29 +158,31 @@ hipError_t launch_rescore(int dtype, const void* W, const void* H, const int32_t
   return hipGetLastError();
 }
 
-hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, const float* raw,
-                        const void* P, const void* Z, int K, int64_t V, int64_t B, int k, const void* W,
-                        const void* H, int d, int32_t* idx, float* score, float* logits, hipStream_t stream) {
+hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, bool rowmajor,
+                        const float* raw, const void* P, const void* Z, int K, int64_t V, int64_t B, int k,
+                        const void* W, const void* H, int d, int32_t* idx, float* score, float* logits,
+                        hipStream_t stream) {
   if (n < 1 || n > kMaxLists || L < 1 || L > k) return hipErrorInvalidValue;
   if (L < k && !raw && !(P && Z && K >= 32 && K % 32 == 0)) return hipErrorInvalidValue;
   const uint16_t* Pm = static_cast<const uint16_t*>(P);
   const uint16_t* Zm = static_cast<const uint16_t*>(Z);
+  const int bl = rowmajor ? 1 : 0;
   const dim3 block(kMergeThreads);
   if (!logits) {
     const dim3 grid(1, (unsigned)B);
-    hipLaunchKernelGGL((merge_kernel<uint16_t, false>), grid, block, 0, stream, part_s, part_i, n, L, raw, Pm, Zm, K,
-                       V, k, (const uint16_t*)nullptr, (const uint16_t*)nullptr, d, idx, score, logits);
+    hipLaunchKernelGGL((merge_kernel<uint16_t, false>), grid, block, 0, stream, part_s, part_i, n, L, bl, raw, Pm,
+                       Zm, K, V, k, (const uint16_t*)nullptr, (const uint16_t*)nullptr, d, idx, score, logits);
     return hipGetLastError();
   }
   // enough blocks that waves 1..7 of all of them can hold 2k candidates
   const int G = (2 * k + kMergeWaves - 2) / (kMergeWaves - 1);
   const dim3 grid((unsigned)G, (unsigned)B);
   if (dtype == 0)
-    hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, block, 0, stream, part_s, part_i, n, L, raw, Pm, Zm, K,
-                       V, k, (const uint16_t*)W, (const uint16_t*)H, d, idx, score, logits);
+    hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, block, 0, stream, part_s, part_i, n, L, bl, raw, Pm, Zm,
+                       K, V, k, (const uint16_t*)W, (const uint16_t*)H, d, idx, score, logits);
   else
-    hipLaunchKernelGGL((merge_kernel<float, true>), grid, block, 0, stream, part_s, part_i, n, L, raw, Pm, Zm, K, V,
-                       k, (const float*)W, (const float*)H, d, idx, score, logits);
+    hipLaunchKernelGGL((merge_kernel<float, true>), grid, block, 0, stream, part_s, part_i, n, L, bl, raw, Pm, Zm, K,
+                       V, k, (const float*)W, (const float*)H, d, idx, score, logits);
   return hipGetLastError();
 }
 

@@ -52,8 +52,9 @@ hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, in
                               int* part_i, hipStream_t stream, Timing t = {});
 // kRowsMinB to kRowsMaxB draft rows (bf16, power-of-two r >= 32, at most
 // 8192 elements of z in a column tile group): the same slice lists from the
-// matrix-core stream, no raw scores (the merge recomputes a slice it needs
-// more of). From 5 rows on it is the faster pass (cold calls at r = 128,
+// matrix-core stream, row-major (entry j of block x's list for row b at
+// part_[b][x][j]), no raw scores (the merge recomputes a slice it needs more
+// of). From 5 rows on it is the faster pass (cold calls at r = 128,
 // k = 32: 22.9 against 24.7 us at 8 rows, 21.6 against 21.8 at 4, 20.5
 // against 20.0 at 2).
 constexpr int kRowsMinB = 5;
@@ -162,17 +163,19 @@ hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, i
                                Timing t = {});
 
 // ----------------------------------------------------- kernels_merge.hip
-// Merges n sorted lists of L entries per row (part_[row][entry][list],
-// n <= 512) into the k best, to idx / score (score may be NULL). Lists
+// Merges n sorted lists of L entries per row (part_[row][entry][list], or
+// with `rowmajor` part_[row][list][entry]; n <= 512) into the k best, to
+// idx / score (score may be NULL). Lists
 // shorter than k (L < k) come with the rows' raw scores (raw[row][v], list p
 // holding the best of the slice [V*p/n, V*(p+1)/n)), or, with raw NULL, with
 // P (V x K) and Z (B x K), bf16, from which the merge recomputes the scores
 // of a slice it needs (lists from the matrix-core stream only); with L == k
 // all three may be NULL. With logits != NULL, also writes the winners'
 // exact logits W[id] . h_b.
-hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, const float* raw,
-                        const void* P, const void* Z, int K, int64_t V, int64_t B, int k, const void* W,
-                        const void* H, int d, int32_t* idx, float* score, float* logits, hipStream_t stream);
+hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, bool rowmajor,
+                        const float* raw, const void* P, const void* Z, int K, int64_t V, int64_t B, int k,
+                        const void* W, const void* H, int d, int32_t* idx, float* score, float* logits,
+                        hipStream_t stream);
 
 // ---------------------------------------------------- kernels_branch.hip
 // Softmax of each row's k candidate logits, the nb most probable as

@@ -245,14 +245,14 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   }
   if (rows && B >= kRowsRescoreApart) {
     // the merge ranks only; the winners' logits come from their own launch
-    LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, raw, h->P, h->z, (int)h->r, h->V, B,
-                              k, nullptr, nullptr, (int)h->d, idx, score, nullptr, s),
+    LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, true, raw, h->P, h->z, (int)h->r,
+                              h->V, B, k, nullptr, nullptr, (int)h->d, idx, score, nullptr, s),
             "merge launch");
     if (logits)
       LRH_HIP(lrh::launch_rescore(h->dtype, h->W, H, idx, B, k, h->V, (int)h->d, logits, s), "rescore launch");
     return LRHEAD_OK;
   }
-  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, raw, rows ? h->P : nullptr,
+  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, rows, raw, rows ? h->P : nullptr,
                             rows ? h->z : nullptr, (int)h->r, h->V, B, k, h->W, H, (int)h->d, idx, score, logits,
                             s),
           "merge launch");
@@ -421,8 +421,8 @@ int fullhead_topk(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, flo
                                timing(h)),
             "full-head selection launch");
   }
-  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, k, nullptr, nullptr, nullptr, 0, h->V, B, k,
-                            nullptr, nullptr, (int)h->d, idx, logits, nullptr, s),
+  LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, k, false, nullptr, nullptr, nullptr, 0, h->V, B,
+                            k, nullptr, nullptr, (int)h->d, idx, logits, nullptr, s),
           "merge launch");
   return LRHEAD_OK;
 }

@@ -173,8 +173,7 @@ __device__ __forceinline__ float recompute64(const RowScores& src, int64_t c0, i
 }
 
 // Steps 1-2 of the merge of row b, by all 512 threads: list p (p < n <= 512)
-// is read by thread p; entry j of list p sits at lists_s/i[j * n + p] (the
-// row's depth-major block). src (raw and P both NULL when L >= k) gives the
+// is read by thread p; entry j of list p sits at lists_s/i[lay.at(j, p)]. src (raw and P both NULL when L >= k) gives the
 // row's scores, slice p being [V*p/n, V*(p+1)/n). Returns the candidate
 // count (past kCandSlots: the buffer overflowed and only the count is right).
 //
@@ -186,8 +185,8 @@ __device__ __forceinline__ float recompute64(const RowScores& src, int64_t c0, i
 // images, so at least k entries reach T. With k heads or fewer, T = 1 and
 // every non-empty entry counts.
 __device__ __forceinline__ int merge_collect(MergeSmem& m, const float* __restrict__ lists_s,
-                                             const int* __restrict__ lists_i, int n, int L, const RowScores& src,
-                                             int64_t V, int k) {
+                                             const int* __restrict__ lists_i, int n, int L, ListLayout lay,
+                                             const RowScores& src, int64_t V, int k) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int F = min(kFront, L);
   const int p = threadIdx.x;
@@ -197,8 +196,8 @@ __device__ __forceinline__ int merge_collect(MergeSmem& m, const float* __restri
 #pragma unroll
   for (int j = 0; j < kFront; ++j) {
     const int jc = min(j, L - 1);
-    fs[j] = lists_s[(int64_t)jc * n + pc];
-    fi[j] = lists_i[(int64_t)jc * n + pc];
+    fs[j] = lists_s[lay.at(jc, pc)];
+    fi[j] = lists_i[lay.at(jc, pc)];
     if (p >= n || j >= L) fi[j] = kSentinelId;
   }
   // score images (order-preserving, -0 as +0); 0 marks an empty entry
@@ -300,8 +299,8 @@ __device__ __forceinline__ int merge_collect(MergeSmem& m, const float* __restri
         for (int j0 = F; j0 < L; j0 += kWave) {
           const int j = j0 + lane;
           const int jc = min(j, L - 1);
-          const float sc = lists_s[(int64_t)jc * n + q];
-          const int id = j < L ? lists_i[(int64_t)jc * n + q] : kSentinelId;
+          const float sc = lists_s[lay.at(jc, q)];
+          const int id = j < L ? lists_i[lay.at(jc, q)] : kSentinelId;
           push_cands(m, reaches(sc, id), cand_key(sc, id));
         }
       } else {

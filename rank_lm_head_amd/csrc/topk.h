@@ -493,25 +493,34 @@ __device__ __forceinline__ void wave_top_few(const float* sc, int n, int id0, in
 }
 
 // ------------------------------------------------------- sequential merge
+// Where entry j of list p of a row's n sorted lists sits: depth-major (entry
+// j of all lists together: entry stride n, list stride 1) or row-major (a
+// list's entries together: entry stride 1, list stride = its length).
+struct ListLayout {
+  int64_t entry_stride, list_stride;
+  __device__ __forceinline__ int64_t at(int j, int p) const { return j * entry_stride + p * list_stride; }
+};
+
 // Wave-wide fallback: folds every list into (s, i), the running best 64 in
 // candidate order, skipping lists whose best entry does not beat the running
-// k-th. Lists are depth-major: entry j of list p at [j * n + p].
-__device__ __forceinline__ void merge_lists_seq(const float* ps, const int* pi, int n, int k, float& s, int& i) {
+// k-th.
+__device__ __forceinline__ void merge_lists_seq(const float* ps, const int* pi, int n, int k, ListLayout lay,
+                                                float& s, int& i) {
   const int lane = threadIdx.x & 63;
   s = neg_inf();
   i = kSentinelId;
   const int j = kWave - 1 - lane;
   for (int p = 0; p < n; ++p) {
-    const float head = ps[p];
-    const int head_i = pi[p];
+    const float head = ps[lay.at(0, p)];
+    const int head_i = pi[lay.at(0, p)];
     const float ks = readlane_f(s, k - 1);
     const int ki = __builtin_amdgcn_readlane(i, k - 1);
     if (!precedes(head, head_i, ks, ki)) continue;
     float os = neg_inf();
     int oi = kSentinelId;
     if (j < k) {
-      os = ps[(int64_t)j * n + p];
-      oi = pi[(int64_t)j * n + p];
+      os = ps[lay.at(j, p)];
+      oi = pi[lay.at(j, p)];
     }
     merge_reversed(s, i, os, oi);
   }
