@@ -53,17 +53,20 @@ __global__ void __launch_bounds__(256) rescore_kernel(const T* __restrict__ W, c
 //     entries that reach T to the candidate buffer. Only a list whose 4th
 //     entry still reaches T can hold more candidates; those (rare) lists are
 //     read further, one per wave.
-//  3. Wave 0 ranks the candidates. Meanwhile, when there are few enough
-//     candidates, waves 1..7 of the G blocks already compute the logits of
-//     all of them, so the W rows are in flight during the selection: a
-//     candidate with token id v belongs to block v % G (the blocks' buffers
-//     hold the same candidates in different orders, the ids agree), and the
-//     block's waves take its candidates in turn. Afterwards each block
-//     writes the logits of the winners that belong to it. With more
-//     candidates, wave w of block g rescores winner g*per + w instead.
+//  3. Wave 0 ranks the candidates. Meanwhile, with `speculate` and few
+//     enough candidates, waves 1..7 of the G blocks already compute the
+//     logits of all of them, so the W rows are in flight during the
+//     selection: a candidate with token id v belongs to block v % G (the
+//     blocks' buffers hold the same candidates in different orders, the ids
+//     agree), and the block's waves take its candidates in turn. Afterwards
+//     each block writes the logits of the winners that belong to it.
+//     Otherwise block g's waves rescore winners g*per .. (g+1)*per - 1 after
+//     the ranking, one per wave at a time. Speculation reads W rows of a few
+//     more candidates than k: worth it when the call is latency-bound (few
+//     rows), not when many rows already keep the chip busy.
 template <typename T, bool RESCORE>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
-    const float* __restrict__ part_s, const int* __restrict__ part_i, int n, int L, int rowmajor,
+    const float* __restrict__ part_s, const int* __restrict__ part_i, int n, int L, int rowmajor, int speculate,
     const float* __restrict__ raw, const uint16_t* __restrict__ P, const uint16_t* __restrict__ Z, int K, int64_t V,
     int k,
     const T* __restrict__ W, const T* __restrict__ H, int d, int32_t* __restrict__ idx, float* __restrict__ score,
@@ -81,7 +84,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
 
   // 3. selection, with the rescoring in flight when it can be
   const bool fits = nc <= kCandSlots;
-  const bool spec = RESCORE && fits && nc <= G * (kMergeWaves - 1);
+  const bool spec = RESCORE && speculate && fits && nc <= G * (kMergeWaves - 1);
   if (wave == 0) {
     if (fits) {
       select_candidates(m, nc, k);
@@ -132,8 +135,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(
       }
     } else {
       const int per = (k + G - 1) / G;
-      const int j = g * per + wave;
-      if (wave < per && j < k) {
+      const int j1 = min(k, (g + 1) * per);
+      for (int j = g * per + wave; j < j1; j += kMergeWaves) {
         const int v = m.top_i[j];
         float acc = __builtin_nanf("");
         if (v >= 0 && v < V) acc = wave_row_dot<T>(W + (int64_t)v * d, H + b * (int64_t)d, d);
@@ -161,27 +164,28 @@ hipError_t launch_rescore(int dtype, const void* W, const void* H, const int32_t
 hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, bool rowmajor,
                         const float* raw, const void* P, const void* Z, int K, int64_t V, int64_t B, int k,
                         const void* W, const void* H, int d, int32_t* idx, float* score, float* logits,
-                        hipStream_t stream) {
+                        bool speculate, hipStream_t stream) {
   if (n < 1 || n > kMaxLists || L < 1 || L > k) return hipErrorInvalidValue;
   if (L < k && !raw && !(P && Z && K >= 32 && K % 32 == 0)) return hipErrorInvalidValue;
   const uint16_t* Pm = static_cast<const uint16_t*>(P);
   const uint16_t* Zm = static_cast<const uint16_t*>(Z);
-  const int bl = rowmajor ? 1 : 0;
+  const int bl = rowmajor ? 1 : 0, sp = speculate ? 1 : 0;
   const dim3 block(kMergeThreads);
   if (!logits) {
     const dim3 grid(1, (unsigned)B);
-    hipLaunchKernelGGL((merge_kernel<uint16_t, false>), grid, block, 0, stream, part_s, part_i, n, L, bl, raw, Pm,
+    hipLaunchKernelGGL((merge_kernel<uint16_t, false>), grid, block, 0, stream, part_s, part_i, n, L, bl, sp, raw, Pm,
                        Zm, K, V, k, (const uint16_t*)nullptr, (const uint16_t*)nullptr, d, idx, score, logits);
     return hipGetLastError();
   }
-  // enough blocks that waves 1..7 of all of them can hold 2k candidates
-  const int G = (2 * k + kMergeWaves - 2) / (kMergeWaves - 1);
+  // speculative: enough blocks that waves 1..7 of all of them can hold 2k
+  // candidates; otherwise one winner per wave
+  const int G = speculate ? (2 * k + kMergeWaves - 2) / (kMergeWaves - 1) : (k + kMergeWaves - 1) / kMergeWaves;
   const dim3 grid((unsigned)G, (unsigned)B);
   if (dtype == 0)
-    hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, block, 0, stream, part_s, part_i, n, L, bl, raw, Pm, Zm,
+    hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, block, 0, stream, part_s, part_i, n, L, bl, sp, raw, Pm, Zm,
                        K, V, k, (const uint16_t*)W, (const uint16_t*)H, d, idx, score, logits);
   else
-    hipLaunchKernelGGL((merge_kernel<float, true>), grid, block, 0, stream, part_s, part_i, n, L, bl, raw, Pm, Zm, K,
+    hipLaunchKernelGGL((merge_kernel<float, true>), grid, block, 0, stream, part_s, part_i, n, L, bl, sp, raw, Pm, Zm, K,
                        V, k, (const float*)W, (const float*)H, d, idx, score, logits);
   return hipGetLastError();
 }

@@ -171,11 +171,12 @@ hipError_t launch_batch_select(const void* M, const void* X, int64_t V, int K, i
 // P (V x K) and Z (B x K), bf16, from which the merge recomputes the scores
 // of a slice it needs (lists from the matrix-core stream only); with L == k
 // all three may be NULL. With logits != NULL, also writes the winners'
-// exact logits W[id] . h_b.
+// exact logits W[id] . h_b, with `speculate` starting on the candidates'
+// logits while the winners are ranked.
 hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, bool rowmajor,
                         const float* raw, const void* P, const void* Z, int K, int64_t V, int64_t B, int k,
                         const void* W, const void* H, int d, int32_t* idx, float* score, float* logits,
-                        hipStream_t stream);
+                        bool speculate, hipStream_t stream);
 
 // ---------------------------------------------------- kernels_branch.hip
 // Softmax of each row's k candidate logits, the nb most probable as

@@ -47,12 +47,14 @@ namespace {
 constexpr uint32_t kMagic = 0x4c524844u;  // "LRHD"
 constexpr int64_t kDownGemmRows = 256;     // rows from which z = Q . h may run on the GEMM kernel
 constexpr int64_t kDownSplitMaxElems = 65536;   // ... when B * r is above this
-// From this many rows on, the 9-64 row path ranks in the merge and rescores
-// the winners in a launch of their own: the merge's speculative rescoring of
-// every candidate (a few more than k per row) reads more of W than it hides
-// (cold calls at r = 128, k = 32: 31.2 against 30.1 us at 32 rows, 44.2
-// against 39.7 at 64; 27.3 against 29.1 at 24).
-constexpr int64_t kRowsRescoreApart = 32;
+// From this many rows on, the merge rescores only the winners, after the
+// ranking: its speculative rescoring of every candidate (a few more than k
+// per row) reads more of W than it hides once many rows keep the chip busy
+// (cold calls at r = 128, k = 32, speculative against not: 45.5 against
+// 38.6 us at 64 rows, 31.9 against 28.9 at 32, 27.3 against 28.0 at 24,
+// 23.9 against 24.8 at 16). (A separate rescoring launch after a ranking-
+// only merge measured 40.1 us at 64 rows.)
+constexpr int64_t kSpeculateBelow = 32;
 constexpr int64_t kBMaxLimit = int64_t(1) << 20;
 
 thread_local char g_err[512] = "";
@@ -243,18 +245,9 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
                                timing(h)),
             "score/selection launch");
   }
-  if (rows && B >= kRowsRescoreApart) {
-    // the merge ranks only; the winners' logits come from their own launch
-    LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, true, raw, h->P, h->z, (int)h->r,
-                              h->V, B, k, nullptr, nullptr, (int)h->d, idx, score, nullptr, s),
-            "merge launch");
-    if (logits)
-      LRH_HIP(lrh::launch_rescore(h->dtype, h->W, H, idx, B, k, h->V, (int)h->d, logits, s), "rescore launch");
-    return LRHEAD_OK;
-  }
   LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, rows, raw, rows ? h->P : nullptr,
                             rows ? h->z : nullptr, (int)h->r, h->V, B, k, h->W, H, (int)h->d, idx, score, logits,
-                            s),
+                            B < kSpeculateBelow, s),
           "merge launch");
   return LRHEAD_OK;
 }
@@ -422,7 +415,7 @@ int fullhead_topk(lrhead_t h, const void* H, int64_t B, int k, int32_t* idx, flo
             "full-head selection launch");
   }
   LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, k, false, nullptr, nullptr, nullptr, 0, h->V, B,
-                            k, nullptr, nullptr, (int)h->d, idx, logits, nullptr, s),
+                            k, nullptr, nullptr, (int)h->d, idx, logits, nullptr, false, s),
           "merge launch");
   return LRHEAD_OK;
 }
