@@ -418,6 +418,8 @@ def latency_table(torch, lr, dev, steps: int) -> dict:
                 for h in heads:
                     h.close()
                 del heads, ws, g
+            print(f"[table] r={r} B={B}: {[x['us_per_call'] for x in rows[-len(TABLE_K):]]}", file=sys.stderr,
+                  flush=True)
         del sets, W
         torch.cuda.empty_cache()
     return {"table": "draft-head call latency, cache-cold graph replay", "V": TABLE_V, "d": TABLE_D,
