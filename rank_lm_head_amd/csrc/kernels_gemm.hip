@@ -58,7 +58,7 @@ struct GemmCfg {
   static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the loaders");
 };
 
-enum { kModeMax = 0, kModeFilter = 1, kModeStore = 2 };
+enum { kModeMax = 0, kModeFilter = 1, kModeStore = 2, kModePartial = 3 };
 
 __device__ __forceinline__ int swz(int row, int c) { return row * kRowChunks + (c ^ (row & 7)); }
 
@@ -154,7 +154,12 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
     int64_t ldS, uint32_t* __restrict__ mask, int NW) {
   extern __shared__ u32x4 lds[];
   constexpr int SA = C::BM * kRowChunks, SB = C::BN * kRowChunks;   // 16-byte chunks per stage
-  const int nbuf = min(C::ST, (K + kBK - 1) / kBK);   // stage buffers (fewer for short K)
+  // K stages [kb, kb + nk) of the nk_all: all of them, or with kModePartial
+  // the blockIdx.y-th of gridDim.y equal shares
+  const int nk_all = (K + kBK - 1) / kBK;
+  const int kb = MODE == kModePartial ? (int)((int64_t)nk_all * blockIdx.y / gridDim.y) : 0;
+  const int nk = MODE == kModePartial ? (int)((int64_t)nk_all * (blockIdx.y + 1) / gridDim.y) - kb : nk_all;
+  const int nbuf = max(1, min(C::ST, nk));   // stage buffers (fewer for short K)
   u32x4* As = lds;                  // [nbuf][SA]
   u32x4* Bs = lds + nbuf * SA;      // [nbuf][SB]
 
@@ -184,8 +189,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
 #pragma unroll
     for (int jn = 0; jn < C::FN; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (K + kBK - 1) / kBK;
-  const bool ktail = (K % kBK) != 0;
+  const bool ktail = (K % kBK) != 0;   // the last of all stages is partial
   StageDma<C::A_LD> la;
   StageDma<C::B_LD> lb;
   la.init(M, m0, V, K, C::BM);
@@ -196,8 +200,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
 #pragma unroll
   for (int st = 0; st < C::ST - 1; ++st) {
     if (st < nk) {
-      la.issue(As + st * SA, st, K, ktail && st == nk - 1);
-      lb.issue(Bs + st * SB, st, K, ktail && st == nk - 1);
+      la.issue(As + st * SA, kb + st, K, ktail && kb + st == nk_all - 1);
+      lb.issue(Bs + st * SB, kb + st, K, ktail && kb + st == nk_all - 1);
     }
   }
   for (int kc = 0; kc < nk; ++kc) {
@@ -211,8 +215,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
     if (kc + C::ST - 1 < nk) {
       const int nx = kc + C::ST - 1;
       const int nb = nx % nbuf;
-      la.issue(As + nb * SA, nx, K, ktail && nx == nk - 1);
-      lb.issue(Bs + nb * SB, nx, K, ktail && nx == nk - 1);
+      la.issue(As + nb * SA, kb + nx, K, ktail && kb + nx == nk_all - 1);
+      lb.issue(Bs + nb * SB, kb + nx, K, ktail && kb + nx == nk_all - 1);
     }
     const u32x4* as = As + (kc % nbuf) * SA;
     const u32x4* bs = Bs + (kc % nbuf) * SB;
@@ -259,6 +263,26 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_sel_kernel(
             if (vrow + i * 16 + q < V) m = fmaxf(m, acc[i][jn][q]);
         m = fmax_lanes(m);
         if (g == 0 && n < B) aux_f[n * ns_tiles + vb_local * (C::BM / 32) + wm * (C::FM / 2) + i2] = m;
+      }
+    }
+  } else if constexpr (MODE == kModePartial) {
+    // fp32 partial products of this block's K stages: row n of part
+    // blockIdx.y at S + (blockIdx.y * B + n) * ldS
+#pragma unroll
+    for (int jn = 0; jn < C::FN; ++jn) {
+      const int64_t n = n0 + wn * C::TN + jn * 16 + col;
+      if (n >= B) continue;
+      float* prow = S + ((int64_t)blockIdx.y * B + n) * ldS;
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) {
+        const int64_t m = vrow + i * 16;
+        if (m + 4 <= V) {
+          *reinterpret_cast<f32x4*>(prow + m) = acc[i][jn];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (m + q < V) prow[m + q] = acc[i][jn][q];
+        }
       }
     }
   } else if constexpr (MODE == kModeStore) {
@@ -850,7 +874,7 @@ size_t gemm_lds_bytes(int K = 1 << 30) {
 template <class C>
 hipError_t allow_lds() {
   for (const void* f : {(const void*)gemm_sel_kernel<C, kModeMax>, (const void*)gemm_sel_kernel<C, kModeFilter>,
-                        (const void*)gemm_sel_kernel<C, kModeStore>}) {
+                        (const void*)gemm_sel_kernel<C, kModeStore>, (const void*)gemm_sel_kernel<C, kModePartial>}) {
     const hipError_t e =
         hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)gemm_lds_bytes<C>());
     if (e != hipSuccess) return e;
@@ -861,12 +885,15 @@ hipError_t allow_lds() {
 template <class C>
 hipError_t run_gemm(int mode, const uint16_t* M, const uint16_t* X, int64_t V, int K, int64_t B, int nvb,
                     int stride, float* tmax, int ns_tiles, const float* theta, float* S, int64_t ldS,
-                    uint32_t* mask, int NW, hipStream_t stream, Timing t = {}) {
+                    uint32_t* mask, int NW, hipStream_t stream, Timing t = {}, int ksplit = 1) {
   const int64_t NT = (B + C::BN - 1) / C::BN;
   const int64_t nvb_pad = nvb >= kXcds ? (nvb + kXcds - 1) / kXcds * kXcds : nvb;
-  const dim3 grid((unsigned)(nvb_pad * NT));
+  const dim3 grid((unsigned)(nvb_pad * NT), (unsigned)(mode == kModePartial ? ksplit : 1));
   const size_t lds = gemm_lds_bytes<C>(K);
-  if (mode == kModeMax)
+  if (mode == kModePartial)
+    hipLaunchKernelGGL((gemm_sel_kernel<C, kModePartial>), grid, dim3(kGemmThreads), lds, stream, M, X, V, K, B,
+                       nvb, stride, tmax, ns_tiles, theta, S, ldS, mask, NW);
+  else if (mode == kModeMax)
     hipLaunchKernelGGL((gemm_sel_kernel<C, kModeMax>), grid, dim3(kGemmThreads), lds, stream, M, X, V, K, B, nvb,
                        stride, tmax, ns_tiles, theta, S, ldS, mask, NW);
   else if (mode == kModeStore)
@@ -1024,10 +1051,28 @@ hipError_t batch_init() {
   return e;
 }
 
-hipError_t launch_down_gemm(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream) {
+hipError_t launch_down_gemm(const void* Q, const void* H, int r, int d, int64_t B, void* Z, float* part,
+                            size_t part_bytes, hipStream_t stream) {
   const int nvb = (r + CfgDown::BM - 1) / CfgDown::BM;
-  return run_gemm<CfgDown>(kModeStore, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(H), r, d, B,
-                           nvb, 1, nullptr, 0, nullptr, static_cast<float*>(Z), r, nullptr, 0, stream);
+  const auto* q = static_cast<const uint16_t*>(Q);
+  const auto* h = static_cast<const uint16_t*>(H);
+  // K split over blocks until the grid has about 512 of them (at least 4
+  // K stages each); the parts are added in a fixed order by down_reduce.
+  // At 2048 rows, r = 256, d = 5120 (128 tiles): one block per tile took
+  // 34.6 us; 2, 4, 8 and 16 parts 25.9, 23.8, 25.4 and 30.7 us with the
+  // reduction (the tiles re-read H from L2, which more parts do not change).
+  const int64_t tiles = (nvb >= kXcds ? (nvb + kXcds - 1) / kXcds * kXcds : nvb) *
+                        ((B + CfgDown::BN - 1) / CfgDown::BN);
+  const int nk = (d + kBK - 1) / kBK;
+  int split = (int)std::min<int64_t>((512 + tiles - 1) / tiles, nk / 4);
+  while (split > 1 && size_t(split) * size_t(B) * size_t(r) * 4 > part_bytes) --split;
+  if (split <= 1)
+    return run_gemm<CfgDown>(kModeStore, q, h, r, d, B, nvb, 1, nullptr, 0, nullptr, static_cast<float*>(Z), r,
+                             nullptr, 0, stream);
+  hipError_t e = run_gemm<CfgDown>(kModePartial, q, h, r, d, B, nvb, 1, nullptr, 0, nullptr, part, r, nullptr, 0,
+                                   stream, {}, split);
+  if (e != hipSuccess) return e;
+  return launch_down_reduce(part, split, B * r, Z, stream);
 }
 
 BatchPlan plan_batch(int64_t V, int64_t B, int k) {

@@ -350,6 +350,12 @@ hipError_t launch_down_split(const void* Q, const void* H, int r, int d, int64_t
   return hipGetLastError();
 }
 
+hipError_t launch_down_reduce(const float* part, int S, int64_t n, void* Z, hipStream_t stream) {
+  hipLaunchKernelGGL(down_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, part, S, n,
+                     (uint16_t*)Z);
+  return hipGetLastError();
+}
+
 hipError_t launch_select(int dtype, const void* M, const void* X, int64_t V, int K, int64_t B, int k,
                          int n_vsplit, float* part_s, int* part_i, hipStream_t stream, Timing t) {
   dim3 grid(n_vsplit, (unsigned)((B + kTile - 1) / kTile));

@@ -113,6 +113,8 @@ hipError_t launch_down(int dtype, const void* Q, const void* H, int r, int d, in
 // sums (down_split_parts(d) x B x r) in `part`, then a reduction in a fixed
 // order and the rounding to bf16.
 int down_split_parts(int d);
+// Adds S partial sums part[s][i] (i < n) in s order and rounds to bf16: Z[i].
+hipError_t launch_down_reduce(const float* part, int S, int64_t n, void* Z, hipStream_t stream);
 hipError_t launch_down_split(const void* Q, const void* H, int r, int d, int64_t B, void* Z, float* part,
                              hipStream_t stream);
 
@@ -152,8 +154,12 @@ size_t batch_scratch_bytes(int64_t V, int64_t B_max);
 BatchScratch batch_scratch(void* base, int64_t V, int64_t B_max);
 // Lets the GEMM kernels use more than 64 KiB of LDS (call once per device).
 hipError_t batch_init();
-// z = round_bf16(Q . h) for B rows on the GEMM kernel (bf16 only).
-hipError_t launch_down_gemm(const void* Q, const void* H, int r, int d, int64_t B, void* Z, hipStream_t stream);
+// z = round_bf16(Q . h) for B rows on the GEMM kernel (bf16 only). With
+// too few output tiles to fill the GPU, K is split over blocks (about 512 of
+// them) whose fp32 partial sums go to `part` (when part_bytes holds them)
+// and are added in a fixed order by launch_down_reduce.
+hipError_t launch_down_gemm(const void* Q, const void* H, int r, int d, int64_t B, void* Z, float* part,
+                            size_t part_bytes, hipStream_t stream);
 
 // The k best of every row of X . M^T (M is V x K, X is B x K, bf16) in
 // candidate order to idx / score (score may be NULL). `t` times the main

@@ -210,7 +210,8 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
       LRH_HIP(lrh::launch_down_wide(h->Q, H, (int)h->r, (int)h->d, B, h->z, nullptr, 0, nullptr, 0, s),
               "down-projection launch");
     else if (B >= kDownGemmRows && B * h->r > kDownSplitMaxElems)
-      LRH_HIP(lrh::launch_down_gemm(h->Q, H, (int)h->r, (int)h->d, B, h->z, s), "down-projection launch");
+      LRH_HIP(lrh::launch_down_gemm(h->Q, H, (int)h->r, (int)h->d, B, h->z, h->bw.S, h->bw.S_bytes, s),
+              "down-projection launch");
     else if (part_bytes <= h->bw.S_bytes)
       LRH_HIP(lrh::launch_down_split(h->Q, H, (int)h->r, (int)h->d, B, h->z, h->bw.S, s), "down-projection launch");
     else

@@ -137,6 +137,7 @@ def test_streaming_path_shapes(V, d, r, B, k):
     (30000, 5120, 512, 8, 64),   # eight rows at r = 512 take the matrix-core path
     (100, 64, 16, 300, 8),       # strip kernel: one partial strip (V < 256), two batch tiles
     (3000, 64, 8, 300, 16),      # strip kernel at r = 8: K steps mostly past the row, zero z chunks
+    (3000, 1000, 128, 600, 16),  # z on the GEMM kernel split over K (4 parts), the last K stage partial
 ])
 def test_batch_path_shapes(V, d, r, B, k):
     inp = gen.make_custom(V, d, r, B, "bf16", seed=V + B)
