@@ -155,6 +155,8 @@ def test_batch_path_shapes(V, d, r, B, k):
 
 
 @pytest.mark.parametrize("V,d,r,B,k", [
+    (20, 64, 32, 12, 20),        # one slice of 20 rows, k = V: its 4-entry list is deep, the merge recomputes it
+    (10, 64, 32, 6, 3),          # V below one 16-row tile: every wave's tile is its last, partly past V
     (257, 64, 32, 9, 9),         # two slices of 128 and 129 rows, 16-row column tile with 7 idle rows
     (1000, 136, 32, 12, 5),      # ragged last 16-row tile of every wave
     (300, 1032, 32, 20, 3),      # k < 4: lists of 3
