@@ -8,9 +8,10 @@
 // row the call is bound by reading P once (V x r bf16); what is left around
 // that stream is latency, and this file cuts it to two launches:
 //
-//   down_wide_kernel  z = Q . h for up to 8 rows, one block per row of Q
-//                     (r blocks, each reading a whole row of Q at once), and
-//                     the reset of the score pass's completion counters.
+//   down_wide_kernel  z = Q . h for up to 64 rows, one block per row of Q
+//                     and group of 8 rows (each reading a whole row of Q at
+//                     once), and the reset of the one-row pass's completion
+//                     counters.
 //   draft1_kernel     one block per compute unit streams its vocabulary
 //                     slice of P, takes the slice's best L = min(4, k)
 //                     entries and, speculatively, the exact logit of the

@@ -1,23 +1,25 @@
-// kernels_small.hip — the head for a few rows, bf16: draft calls with B <= 8,
+// kernels_small.hip — the head for a few rows, bf16: draft calls with B <= 64,
 // the full-head baseline with B <= 4.
 //
-// With one to eight rows both contractions are matrix-vector products and
+// With a few rows both contractions are close to matrix-vector products and
 // the time is HBM streaming ("EAGLE-4", section "Retrieve vocabulary
 // candidates cheaply, then score them exactly": the low-rank head still
 // scores every vocabulary row, so P is read once per call). The effort goes
 // to the memory side (large loads, several in flight per wave). The
 // arithmetic is still not free: widening every bf16 element and
 // multiplying it once per row on the vector ALU made the 8-row score pass
-// take 22 us against about 10 for its bytes. So with 2 to 8 rows and r >= 32
-// the scores come from the matrix cores (stream_scores_mfma: half of each
-// 16-column tile idle at 8 rows, which costs nothing here); one row, and
-// the full-head rows, stay on the vector ALU. (The one-row pass on the
+// take 22 us against about 10 for its bytes. So with 2 to 64 rows and r >=
+// 32 the scores come from the matrix cores (stream_mfma_tiles: 16-row column
+// tiles of z, idle columns cost nothing here); one row, and the full-head
+// rows, stay on the vector ALU. (The one-row pass on the
 // matrix cores measured slower, 18.7 against 17.3 us per call at r = 128:
 // its operand tiles turn each 1 KiB wave load into 16 pieces of 64 bytes,
 // and with one row the pass is bound by the memory side alone.)
 //
 //   select_short_kernel s = P . z with the fused k-best of each block's
-//                       slice, for r <= 512 (a power of two)
+//                       slice, scores staged in LDS (2-4 rows; 5-8 at r < 32)
+//   select_rows_kernel  the same for 5-64 rows, the slice lists kept in
+//                       registers
 //   select_long_kernel  the same for rows longer than one wave load (the
 //                       full-head baseline, W . h)
 // z = Q . h comes from down_wide_kernel (kernels_b1.hip). The slice lists are

@@ -1,11 +1,12 @@
-// stream.h — the vocabulary score stream of the few-row (vector ALU) path.
+// stream.h — the vocabulary score stream of the few-row paths.
 //
-// With one to eight draft rows, s[b][v] = P[v,:] . z_b is a matrix-vector
-// product bound by reading P from HBM once ("EAGLE-4", section "Retrieve
-// vocabulary candidates cheaply, then score them exactly": the low-rank
-// head scores every vocabulary row). K/8 lanes hold one vocabulary row (16
-// bytes each), so one wave load is 1 KiB of consecutive rows; every wave
-// keeps two groups of U loads in flight.
+// With a few draft rows, s[b][v] = P[v,:] . z_b is bound by reading P from
+// HBM once ("EAGLE-4", section "Retrieve vocabulary candidates cheaply, then
+// score them exactly": the low-rank head scores every vocabulary row). On
+// the vector ALU (stream_scores) K/8 lanes hold one vocabulary row (16 bytes
+// each), so one wave load is 1 KiB of consecutive rows; every wave keeps two
+// groups of U loads in flight. On the matrix cores (stream_mfma_tiles) the
+// rows go in 16-row tiles against up to four 16-row column tiles of z.
 #pragma once
 
 #include "device.h"
