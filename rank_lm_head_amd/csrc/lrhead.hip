@@ -47,14 +47,15 @@ namespace {
 constexpr uint32_t kMagic = 0x4c524844u;  // "LRHD"
 constexpr int64_t kDownGemmRows = 256;     // rows from which z = Q . h may run on the GEMM kernel
 constexpr int64_t kDownSplitMaxElems = 65536;   // ... when B * r is above this
-// From this many rows on, the merge rescores only the winners, after the
-// ranking: its speculative rescoring of every candidate (a few more than k
-// per row) reads more of W than it hides once many rows keep the chip busy
-// (cold calls at r = 128, k = 32, speculative against not: 45.5 against
-// 38.6 us at 64 rows, 31.9 against 28.9 at 32, 27.3 against 28.0 at 24,
-// 23.9 against 24.8 at 16). (A separate rescoring launch after a ranking-
-// only merge measured 40.1 us at 64 rows.)
-constexpr int64_t kSpeculateBelow = 32;
+// From this many (row, winner) pairs on, the merge rescores only the
+// winners, after the ranking: its speculative rescoring of every candidate
+// (a few more than k per row) reads more of W than it hides once many rows
+// keep the chip busy. Cold calls at r = 128, speculative against not: k = 32:
+// 45.5 against 38.6 us at 64 rows, 31.9 against 28.9 at 32, 27.3 against
+// 28.0 at 24; k = 64: 29.2 against 26.1 at 16 rows, 24.1 against 25.5 at
+// 12; k = 8: 32.6 against 33.7 at 64 rows. (A separate rescoring launch
+// after a ranking-only merge measured 40.1 us at 64 rows, k = 32.)
+constexpr int64_t kSpeculatePairsBelow = 1024;
 constexpr int64_t kBMaxLimit = int64_t(1) << 20;
 
 thread_local char g_err[512] = "";
@@ -248,7 +249,7 @@ int enqueue_head(lrhead_s* h, const void* H, int64_t B, int k, int32_t* idx, flo
   }
   LRH_HIP(lrh::launch_merge(h->dtype, h->part_s, h->part_i, n_lists, list_len, rows, raw, rows ? h->P : nullptr,
                             rows ? h->z : nullptr, (int)h->r, h->V, B, k, h->W, H, (int)h->d, idx, score, logits,
-                            B < kSpeculateBelow, s),
+                            B * k < kSpeculatePairsBelow, s),
           "merge launch");
   return LRHEAD_OK;
 }
