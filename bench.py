@@ -639,9 +639,7 @@ def main() -> int:
     small = cfg.dtype == "bf16" and cfg.B <= 8 and pow2_r
     n_b1 = max(1, min((cfg.V + 63) // 64, N_CU, B1_MAX_BLOCKS))
     one_row = cfg.dtype == "bf16" and cfg.B == 1 and pow2_r and (cfg.V + n_b1 - 1) // n_b1 <= B1_MAX_ROWS_PER_BLOCK
-    col_tile = 16 if cfg.B <= 16 else 32 if cfg.B <= 32 else 64
-    rows = (cfg.dtype == "bf16" and 5 <= cfg.B <= 64 and cfg.r in (32, 64, 128, 256, 512)
-            and col_tile * cfg.r <= 16 * 512 and cfg.V <= 512 * 512)
+    rows = cfg.dtype == "bf16" and 5 <= cfg.B <= 64 and cfg.r in (32, 64, 128, 256, 512) and cfg.V <= 512 * 512
     batch = cfg.dtype == "bf16" and cfg.B > 4 and not small and not rows
     if batch and cfg.r <= 256 and cfg.B > 256:
         sel_kernel, what = "strip_sel_kernel", "main pass: scores of all rows, flagged above the sampled bound"

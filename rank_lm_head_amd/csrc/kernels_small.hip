@@ -126,9 +126,10 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
   }
 }
 
-// ------------------------------------------- score pass, 9 to 64 rows
-// The matrix-core stream (stream_mfma_tiles) with NB/16 column tiles of z,
-// and no score leaves the registers: each lane keeps, for each of its rows
+// ------------------------------------------- score pass, 5 to 64 rows
+// The matrix-core stream (stream_mfma_tiles) with NB/16 column tiles of z
+// (z's fragments in registers, or in LDS above 64 VGPRs of them), and no
+// score leaves the registers: each lane keeps, for each of its rows
 // of z (16 c + (l & 15) in column tile c), the 4 best of the vocabulary rows
 // it is handed (rows 4 (l >> 4) .. +3 of every 16-row tile of its wave's
 // quarter of the slice), in candidate order. At the end the block merges its
@@ -199,6 +200,16 @@ struct RowsLds {
   int li[kWavesSmall][4][kSliceList][kRow];
 };
 
+// z's fragments for NT column tiles take NT * K / 8 VGPRs; above 64 of them
+// (more rows of z at a larger rank) the block keeps z in LDS instead (chunk
+// j of row b at b * K/8 + (j ^ (b & 15)), so that the 16 rows a fragment
+// read touches sit on different banks) and reads each fragment just before
+// its matrix-core step. The copy shares its LDS with the lists at the end.
+template <int K, int NB>
+constexpr bool rows_z_in_lds() {
+  return NB * K > 16 * 512;
+}
+
 template <int K, int NB>
 __global__ void __launch_bounds__(kSmallThreads) select_rows_kernel(
     const uint16_t* __restrict__ M, const uint16_t* __restrict__ X, int64_t V, int B, int L,
@@ -207,9 +218,23 @@ __global__ void __launch_bounds__(kSmallThreads) select_rows_kernel(
   constexpr int NT = NB / 16;
   constexpr int KS = K / 32;
   constexpr int TG = KS >= 4 ? 1 : 4 / KS;   // about 4 wave loads per group (more measured slower)
-  __shared__ RowsLds<NB> sm;
+  constexpr bool ZL = rows_z_in_lds<K, NB>();
+  constexpr int CH = K / 8;                  // 16-byte chunks of a row of z
+  constexpr size_t kZBytes = ZL ? size_t(NB) * CH * 16 : 0;
+  constexpr size_t kLds = sizeof(RowsLds<NB>) > kZBytes ? sizeof(RowsLds<NB>) : kZBytes;
+  __shared__ __align__(16) unsigned char lds_raw[kLds];
+  RowsLds<NB>& sm = *reinterpret_cast<RowsLds<NB>*>(lds_raw);
+  u32x4* zs = reinterpret_cast<u32x4*>(lds_raw);
   const int wave = wave_id(), lane = threadIdx.x & 63;
   const int g = lane >> 4, col = lane & 15;
+  if constexpr (ZL) {
+    static_assert(CH >= 16, "the swizzle stays inside the row");
+    for (int e = threadIdx.x; e < NB * CH; e += kSmallThreads) {
+      const int b = e / CH, j = e % CH;
+      zs[b * CH + (j ^ (b & 15))] = b < B ? load16(X + (int64_t)b * K + j * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+  }
 
   // slice bounds V*x/n in 32 bits: this path keeps V*n below 2^32
   const uint32_t v32 = (uint32_t)V, n32 = gridDim.x;
@@ -230,7 +255,7 @@ __global__ void __launch_bounds__(kSmallThreads) select_rows_kernel(
   // keeps only its rows below whi
   const int whi32 = (int)whi;
   // (the column tiles' lists are independent: interleaved for the scheduler)
-  stream_mfma_tiles<K, NT, TG>(M, X, B, wlo, whi, [&](int64_t base, const f32x4 (&acc)[NT]) {
+  auto sink = [&](int64_t base, const f32x4 (&acc)[NT]) {
     const int row0 = (int)base + 4 * g;
     if ((int)base + 16 <= whi32) {
 #pragma unroll
@@ -245,7 +270,14 @@ __global__ void __launch_bounds__(kSmallThreads) select_rows_kernel(
           for (int c = 0; c < NT; ++c) list_insert4(ts[c], ti[c], acc[c][q], row0 + q);
         }
     }
-  });
+  };
+  if constexpr (ZL) {
+    stream_mfma_tiles_x<K, NT, TG, true>(
+        M, wlo, whi, [&](int c, int t) { return zs[(c * 16 + col) * CH + ((t * 4 + g) ^ col)]; }, sink);
+    __syncthreads();   // the lists below reuse z's LDS
+  } else {
+    stream_mfma_tiles<K, NT, TG>(M, X, B, wlo, whi, sink);
+  }
 
   // the 16 lists of each row of z (4 waves x 4 lane groups) to LDS; then T
   // consecutive lanes per row of z (T = 256 / NB: 4, 8 or 16, inside one
@@ -444,14 +476,12 @@ static int row_loads(int K) {
 
 int small_list_len(int k) { return k < kSliceList ? k : kSliceList; }
 
-// 5 to 64 rows: column tiles of 16, 32 or 64 rows of z; the fragments of z
-// held in registers (NB/16 x K/32 of 16 bytes a lane) stay at 64 VGPRs.
+// 5 to 64 rows: column tiles of 16, 32 or 64 rows of z, their fragments in
+// registers up to 64 VGPRs, else in LDS.
 bool rows_path(int dtype, int64_t B, int64_t K_lowrank, int64_t V) {
   if (dtype != 0 || B < kRowsMinB || B > kRowsMaxB) return false;
   if (V > (int64_t)kMaxSmallBlocks * kBlockRows) return false;
-  if (K_lowrank < 32 || K_lowrank > 512 || (K_lowrank & (K_lowrank - 1)) != 0) return false;
-  const int64_t nb = B <= 16 ? 16 : B <= 32 ? 32 : 64;
-  return nb * K_lowrank <= 16 * 512;
+  return K_lowrank >= 32 && K_lowrank <= 512 && (K_lowrank & (K_lowrank - 1)) == 0;
 }
 
 template <int K>
@@ -464,15 +494,12 @@ static hipError_t launch_rows_k(const void* M, const void* X, int64_t V, int64_t
 #define LRH_RW(NB)                                                                                        \
   LRH_LAUNCH(t, (select_rows_kernel<K, NB>), grid, block, 0, stream, (const uint16_t*)M, (const uint16_t*)X, V, \
              (int)B, L, ps, pi)
-  if (B <= 16) {
+  if (B <= 16)
     LRH_RW(16);
-  } else if constexpr (K <= 256) {
-    if (B <= 32) {
-      LRH_RW(32);
-    } else if constexpr (K <= 128) {
-      LRH_RW(64);
-    }
-  }
+  else if (B <= 32)
+    LRH_RW(32);
+  else
+    LRH_RW(64);
 #undef LRH_RW
   return hipGetLastError();
 }

@@ -50,11 +50,10 @@ hipError_t launch_select_small(const void* M, const void* X, int64_t V, int K, i
                                int* part_i, float* raw, hipStream_t stream, Timing t = {});
 hipError_t launch_select_long(const void* M, const void* X, int64_t V, int K, int64_t B, int k, float* part_s,
                               int* part_i, hipStream_t stream, Timing t = {});
-// kRowsMinB to kRowsMaxB draft rows (bf16, power-of-two r >= 32, at most
-// 8192 elements of z in a column tile group): the same slice lists from the
-// matrix-core stream, row-major (entry j of block x's list for row b at
-// part_[b][x][j]), no raw scores (the merge recomputes a slice it needs more
-// of). From 5 rows on it is the faster pass (cold calls at r = 128,
+// kRowsMinB to kRowsMaxB draft rows (bf16, power-of-two 32 <= r <= 512):
+// the same slice lists from the matrix-core stream, row-major (entry j of
+// block x's list for row b at part_[b][x][j]), no raw scores (the merge
+// recomputes a slice it needs more of). From 5 rows on it is the faster pass (cold calls at r = 128,
 // k = 32: 22.9 against 24.7 us at 8 rows, 21.6 against 21.8 at 4, 20.5
 // against 20.0 at 2).
 constexpr int kRowsMinB = 5;

@@ -98,21 +98,18 @@ __device__ __forceinline__ void stream_scores(const uint16_t* __restrict__ M, co
 // (non-temporal); rows past the wave's range are loaded from its last row (a
 // valid address, so no load is predicated), and the last group prefetches
 // nothing, so no load is outstanding when the function returns.
-template <int K, int NT, int TG, typename Sink>
-__device__ __forceinline__ void stream_mfma_tiles(const uint16_t* __restrict__ M, const uint16_t* __restrict__ X,
-                                                  int B, int64_t wlo, int64_t whi, Sink&& sink) {
+//
+// X's fragments come from xfrag(c, t) (the lane's 16 bytes of k step t of
+// column tile c): stream_mfma_tiles keeps them in registers for the whole
+// pass; stream_mfma_tiles_x takes any accessor (an LDS copy of X when its
+// fragments would take too many registers: XMEM = true).
+template <int K, int NT, int TG, bool XMEM = false, typename XFrag, typename Sink>
+__device__ __forceinline__ void stream_mfma_tiles_x(const uint16_t* __restrict__ M, int64_t wlo, int64_t whi,
+                                                    XFrag&& xfrag, Sink&& sink) {
   static_assert(K % 32 == 0 && NT >= 1 && NT <= 4, "k steps of 32, at most 64 rows of X");
   constexpr int KS = K / 32;   // k steps per tile
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, col = lane & 15;
-  u32x4 xb[NT][KS];
-#pragma unroll
-  for (int c = 0; c < NT; ++c)
-#pragma unroll
-    for (int t = 0; t < KS; ++t) {
-      const int b = c * 16 + col;
-      xb[c][t] = b < B ? load16(X + (int64_t)b * K + t * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
   const int64_t last = whi > 0 ? whi - 1 : 0;
   const int ng = wlo < whi ? (int)((whi - wlo + 16 * TG - 1) / (16 * TG)) : 0;
   u32x4 buf0[TG][KS], buf1[TG][KS];
@@ -126,6 +123,9 @@ __device__ __forceinline__ void stream_mfma_tiles(const uint16_t* __restrict__ M
     }
   };
   auto consume = [&](const u32x4 (&buf)[TG][KS], int64_t base) {
+    // XMEM: xfrag reads memory that does not change; the empty asm keeps
+    // those reads here, not hoisted out of the loop into registers
+    if constexpr (XMEM) asm volatile("" ::: "memory");
 #pragma unroll
     for (int u = 0; u < TG; ++u) {
       f32x4 acc[NT];
@@ -135,7 +135,8 @@ __device__ __forceinline__ void stream_mfma_tiles(const uint16_t* __restrict__ M
 #pragma unroll
         for (int t = 0; t < KS; ++t)
           acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[u][t]),
-                                                           __builtin_bit_cast(bf16x8, xb[c][t]), acc[c], 0, 0, 0);
+                                                           __builtin_bit_cast(bf16x8, xfrag(c, t)), acc[c], 0, 0,
+                                                           0);
       }
       sink(base + u * 16, acc);
     }
@@ -157,6 +158,23 @@ __device__ __forceinline__ void stream_mfma_tiles(const uint16_t* __restrict__ M
   } else if (gi < ng) {
     consume(buf0, wlo + (int64_t)gi * 16 * TG);
   }
+}
+
+template <int K, int NT, int TG, typename Sink>
+__device__ __forceinline__ void stream_mfma_tiles(const uint16_t* __restrict__ M, const uint16_t* __restrict__ X,
+                                                  int B, int64_t wlo, int64_t whi, Sink&& sink) {
+  constexpr int KS = K / 32;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+  u32x4 xb[NT][KS];
+#pragma unroll
+  for (int c = 0; c < NT; ++c)
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const int b = c * 16 + col;
+      xb[c][t] = b < B ? load16(X + (int64_t)b * K + t * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+  stream_mfma_tiles_x<K, NT, TG>(M, wlo, whi, [&](int c, int t) { return xb[c][t]; }, sink);
 }
 
 // The scores of stream_scores on the matrix cores, for 2 to 16 rows (K >=

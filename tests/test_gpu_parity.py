@@ -127,14 +127,14 @@ def test_streaming_path_shapes(V, d, r, B, k):
 
 @pytest.mark.parametrize("V,d,r,B,k", [
     (20000, 256, 96, 130, 48),   # wide batch tile: two row tiles, the second ragged; K tail of 32
-    (6000, 384, 256, 64, 64),    # narrow batch tile exactly full, k = 64
+    (6000, 384, 192, 64, 64),    # narrow batch tile exactly full, k = 64 (r = 192: not the register-list pass)
     (12345, 200, 72, 65, 10),    # one row past the narrow tile; K = 64 + 8
     (257, 64, 16, 9, 9),         # two vocabulary blocks, the second holding one row
     (3000, 200, 72, 300, 16),    # z on the GEMM kernel: r = 64 + 8, d = 3 * 64 + 8, ragged row tile
     (5000, 512, 256, 512, 64),   # z on the GEMM kernel, full tiles
     (40000, 256, 256, 600, 64),  # strip kernel: three batch tiles, strip groups on the XCDs, ragged last strip
     (7000, 5128, 64, 100, 32),   # split down-projection: 11 K parts, the last one 8 columns wide
-    (30000, 5120, 512, 8, 64),   # eight rows at r = 512 take the matrix-core path
+    (30000, 5120, 512, 8, 64),   # eight rows at r = 512 (register-list pass, z in registers)
     (100, 64, 16, 300, 8),       # strip kernel: one partial strip (V < 256), two batch tiles
     (3000, 64, 8, 300, 16),      # strip kernel at r = 8: K steps mostly past the row, zero z chunks
     (3000, 1000, 128, 600, 16),  # z on the GEMM kernel split over K (4 parts), the last K stage partial
@@ -165,6 +165,9 @@ def test_batch_path_shapes(V, d, r, B, k):
     (30000, 512, 512, 16, 64),   # r = 512 on one column tile
     (6000, 384, 128, 64, 64),    # 64 rows at r = 128, k = 64
     (200000, 64, 32, 40, 16),    # 391 rows per slice
+    (20000, 512, 256, 64, 32),   # z in LDS: 64 rows at r = 256
+    (5000, 256, 512, 24, 64),    # z in LDS: 32-row column tiles at r = 512
+    (30000, 512, 512, 40, 16),   # z in LDS: 64 rows at r = 512
 ])
 def test_rows_path_shapes(V, d, r, B, k):
     """5 to 64 rows: the matrix-core pass that keeps each slice's best in
@@ -445,7 +448,7 @@ def test_ties_inside_one_slice_go_to_the_lower_ids(B):
     (4096, 256, 32, 1, "fp32", False),     # fp32 (matrix-core slice lists and merge)
     (20000, 512, 128, 40, "bf16", False),  # register-list pass, down-projection in 8-row groups
     (20000, 512, 128, 40, "bf16", True),   # register-list pass, boundary ties: the merge recomputes slices
-    (20000, 512, 256, 40, "bf16", False),  # staged GEMM passes (40 rows at r = 256)
+    (20000, 512, 256, 40, "bf16", False),  # register-list pass with z in LDS (40 rows at r = 256)
     (20000, 512, 128, 300, "bf16", False), # strip kernel (two batch tiles), split down-projection in the score scratch
 ])
 def test_repeat_calls_and_poisoned_workspace_are_bitwise_stable(V, d, r, B, dt, ties):
