@@ -203,7 +203,9 @@ int lrhead_branch(const float* logits, const int32_t* idx, const float* parent,
  *   Y = orth(W . omega);  q times: Z = orth(W^T . Y), Y = orth(W . Z);
  *   P = Y (V x r, orthonormal columns),  Q = Y^T . W (r x d),
  * orth() being CholeskyQR2 with fp64 Gram matrices, so P . Q is W projected
- * onto the captured column space (exactly W when W has rank r).
+ * onto the captured column space (exactly W when W has rank r). With V and
+ * d multiples of 8 the W-sized products run on the bf16 matrix cores, each
+ * fp32 panel taken as the sum of two bf16 halves (within 2^-17 of it).
  * W: V x d bf16; omega: d x r fp32 (the Gaussian test matrix, supplied by the
  * caller); P: V x r and Q: r x d bf16 outputs; all device pointers, 16-byte
  * aligned, row-major. Requirements: 1 <= r <= min(512, d, V), 0 <= q <= 8,

@@ -13,8 +13,11 @@
 // orth() is CholeskyQR2: G = X^T X (accumulated in fp64), its Cholesky
 // factor G = L L^T, X <- X L^-T, twice.
 //
-// Kernels (vector ALU; the contractions are tall-skinny and need fp32 or
-// fp64 operands for the orthonormalisation):
+// The four W-sized products (W . Omega, W^T . Y, W . Z, W^T . Y) run on the
+// bf16 matrix cores when V and d are multiples of 8 (the fp32 panel split
+// into two bf16 halves, below); otherwise, and for the panel-sized products
+// of the orthonormalisation, which need fp32 or fp64 operands, on the vector
+// ALU:
 //   fgemm_kernel    C = op(A) . B for 64 x 64 tiles of C, K in chunks of 16
 //                   staged through LDS, 4 x 4 outputs per thread; A is W
 //                   (bf16) or an fp32 panel, read as is (M x K) or transposed
@@ -441,6 +444,127 @@ __global__ void __launch_bounds__(256) cast_q_kernel(const float* __restrict__ Z
   }
 }
 
+// ------------------------------------------------ matrix-core W products
+// With V and d multiples of 8 the four W-sized products run on the bf16
+// matrix cores (launch_gemm_f32): the fp32 panel B (K x r) is split into two
+// bf16 halves, hi = bf16(B) and lo = bf16(B - hi) (together within 2^-17 of
+// B), and W . B = W . hi + W . lo is one product with 2r rows, accumulated
+// in fp32. The GEMM wants both operands K-contiguous, so the panel goes in
+// transposed (2r x K) and W^T . Y takes W transposed (d x V, once per build).
+
+// At (cols x rows) = A^T for A (rows x cols, bf16; rows and cols multiples
+// of 8): 64 x 64 tiles through LDS, 16-byte loads and stores.
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(const uint16_t* __restrict__ A, int64_t rows,
+                                                             int64_t cols, uint16_t* __restrict__ At) {
+  __shared__ uint16_t t[64][64 + 2];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {   // 512 chunks of 8 per tile
+    const int e = h * 256 + tid, i = e >> 3, j = (e & 7) * 8;
+    const int64_t row = r0 + i, c = c0 + j;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < rows && c < cols) v = *reinterpret_cast<const u32x4*>(A + row * cols + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      t[i][j + 2 * q] = (uint16_t)(v[q] & 0xFFFFu);
+      t[i][j + 2 * q + 1] = (uint16_t)(v[q] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int e = h * 256 + tid, a = e >> 3, b = (e & 7) * 8;   // At row c0 + a, columns r0 + b ..
+    const int64_t orow = c0 + a, ocol = r0 + b;
+    if (orow < cols && ocol < rows) {
+      u32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = (uint32_t)t[b + 2 * q][a] | ((uint32_t)t[b + 2 * q + 1][a] << 16);
+      *reinterpret_cast<u32x4*>(At + orow * rows + ocol) = v;
+    }
+  }
+}
+
+// out (2r x rows, bf16): out[n][k] = hi(X[k][n]), out[r + n][k] = lo(X[k][n])
+// for the fp32 panel X (rows x r); 64 x 64 tiles through LDS.
+__global__ void __launch_bounds__(256) split_t_kernel(const float* __restrict__ X, int64_t rows, int r,
+                                                      uint16_t* __restrict__ out) {
+  __shared__ float t[64][65];
+  const int64_t k0 = (int64_t)blockIdx.x * 64;
+  const int n0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    const int e = h * 256 + tid, kl = e >> 6, nl = e & 63;
+    const int64_t k = k0 + kl;
+    const int n = n0 + nl;
+    t[kl][nl] = k < rows && n < r ? X[k * r + n] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    const int e = h * 256 + tid, nl = e >> 6, kl = e & 63;
+    const int64_t k = k0 + kl;
+    const int n = n0 + nl;
+    if (k < rows && n < r) {
+      const float x = t[kl][nl];
+      const uint16_t hi = to_bf16(x);
+      const uint16_t lo = to_bf16(x - __uint_as_float((uint32_t)hi << 16));
+      out[(int64_t)n * rows + k] = hi;
+      out[(int64_t)(r + n) * rows + k] = lo;
+    }
+  }
+}
+
+// out (M x r, fp32): out[m][n] = sum over the parts p, in order, of
+// S[p][n][m] + S[p][r + n][m] (S: parts x 2r x M, the GEMM's partial
+// products of the two halves); 64 x 64 tiles through LDS.
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ S, int parts, int r, int64_t M,
+                                                      float* __restrict__ out) {
+  __shared__ float t[64][65];
+  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  const int n0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  const int64_t plane = 2 * (int64_t)r * M;
+#pragma unroll 4
+  for (int h = 0; h < 16; ++h) {
+    const int e = h * 256 + tid, nl = e >> 6, ml = e & 63;
+    const int64_t m = m0 + ml;
+    const int n = n0 + nl;
+    float acc = 0.f;
+    if (m < M && n < r) {
+      for (int p = 0; p < parts; ++p) {
+        const float* sp = S + p * plane;
+        acc += sp[(int64_t)n * M + m] + sp[(int64_t)(r + n) * M + m];
+      }
+    }
+    t[nl][ml] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    const int e = h * 256 + tid, ml = e >> 6, nl = e & 63;
+    const int64_t m = m0 + ml;
+    const int n = n0 + nl;
+    if (m < M && n < r) out[m * r + n] = t[nl][ml];
+  }
+}
+
+// K splits of the W^T . Y product (M = d rows of W^T, K = V): about 512
+// blocks of the GEMM, at least 4 stages of 64 each.
+int wt_splits(int64_t V, int64_t d, int r) {
+  const int64_t bn = 2 * r > 128 ? 256 : 2 * r > 64 ? 128 : 64;
+  const int64_t nt = (2 * r + bn - 1) / bn;
+  int64_t nvb = (d + 255) / 256;
+  if (nvb >= 8) nvb = (nvb + 7) / 8 * 8;
+  const int64_t tiles = nvb * nt;
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t smax = std::max<int64_t>(1, (V + 63) / 64 / 4);
+  return (int)std::min<int64_t>(std::min<int64_t>(s, smax), 64);
+}
+
+bool factor_on_mfma(int64_t V, int64_t d) { return V % 8 == 0 && d % 8 == 0; }
+
 struct FactorWs {
   float* Y[2];      // V x r
   float* Z[2];      // d x r
@@ -449,6 +573,10 @@ struct FactorWs {
   double* G;        // r x r
   float* Rinv;      // r x r
   uint32_t* status;
+  // matrix-core products only
+  uint16_t* Wt;     // d x V
+  uint16_t* Xh;     // 2r x max(V, d): the panel's halves, transposed
+  float* S;         // the GEMM's fp32 products: max(2r x V, splits x 2r x d)
 };
 
 constexpr int kSplitZ = 16;     // splits of K = V for W^T . Y
@@ -479,6 +607,16 @@ size_t ws_layout(int64_t V, int64_t d, int r, FactorWs* w, char* base) {
   t.G = (double*)take((size_t)r * r * 8);
   t.Rinv = (float*)take((size_t)r * r * 4);
   t.status = (uint32_t*)take(256);
+  t.Wt = nullptr;
+  t.Xh = nullptr;
+  t.S = nullptr;
+  if (factor_on_mfma(V, d)) {
+    const int64_t mx = V > d ? V : d;
+    t.Wt = (uint16_t*)take((size_t)d * V * 2);
+    t.Xh = (uint16_t*)take((size_t)2 * r * mx * 2);
+    const size_t s1 = (size_t)2 * r * V, s2 = (size_t)wt_splits(V, d, r) * 2 * r * d;
+    t.S = (float*)take((s1 > s2 ? s1 : s2) * 4);
+  }
   if (w) *w = t;
   return off;
 }
@@ -537,9 +675,32 @@ hipError_t orth(float*& X, float*& T, int64_t rows, int r, const FactorWs& w, hi
   return hipSuccess;
 }
 
+// out (rows_out x r) = A . B on the matrix cores, A given as the bf16 matrix
+// Am (rows_out x K, K-contiguous: W, or W^T for W^T . Y), B the fp32 panel
+// (K x r): the panel's halves transposed, one GEMM over 2r rows (K split in
+// `splits` parts), the parts and halves added in a fixed order.
+hipError_t mfma_times(const uint16_t* Am, int64_t rows_out, int64_t K, int r, const float* B, float* out, int splits,
+                      const FactorWs& w, hipStream_t s) {
+  hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)((K + 63) / 64), (unsigned)((r + 63) / 64)), dim3(256), 0, s, B,
+                     K, r, w.Xh);
+  LRH_F(hipGetLastError());
+  LRH_F(launch_gemm_f32(Am, rows_out, (int)K, w.Xh, 2 * r, w.S, splits, s));
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows_out + 63) / 64), (unsigned)((r + 63) / 64)), dim3(256), 0,
+                     s, w.S, splits, r, rows_out, out);
+  return hipGetLastError();
+}
+
+// Y = W . B (V x r) for the panel B (d x r)
+hipError_t w_times(const uint16_t* W, int64_t V, int64_t d, int r, const float* B, float* Y, const FactorWs& w,
+                   hipStream_t s) {
+  if (w.Wt) return mfma_times(W, V, d, r, B, Y, 1, w, s);
+  return gemm<uint16_t, false, float>(W, d, B, r, Y, (int)V, r, d, 1, s);
+}
+
 // Z = W^T . Y (d x r), reduced into Zout
 hipError_t wt_times(const uint16_t* W, int64_t V, int64_t d, int r, const float* Y, float* Zout, const FactorWs& w,
                     hipStream_t s) {
+  if (w.Wt) return mfma_times(w.Wt, d, V, r, Y, Zout, wt_splits(V, d, r), w, s);
   const int Sz = splits_for(V, kSplitZ);
   LRH_F((gemm<uint16_t, true, float>(W, d, Y, r, w.part, (int)d, r, V, kSplitZ, s)));
   hipLaunchKernelGGL(reduce_kernel<float>, dim3((unsigned)((d * r + 255) / 256)), dim3(256), 0, s, w.part, Sz,
@@ -560,13 +721,18 @@ hipError_t launch_factor(const void* Wv, int64_t V, int64_t d, int r, int q, con
   hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, w.status, 1);
   LRH_F(hipGetLastError());
   float *Y = w.Y[0], *Yt = w.Y[1], *Z = w.Z[0], *Zt = w.Z[1];
+  if (w.Wt) {   // W^T for the matrix-core W^T . Y
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((d + 63) / 64), (unsigned)((V + 63) / 64)), dim3(256),
+                       0, s, W, V, d, w.Wt);
+    LRH_F(hipGetLastError());
+  }
   // Y = orth(W . Omega)
-  LRH_F((gemm<uint16_t, false, float>(W, d, omega, r, Y, (int)V, r, d, 1, s)));
+  LRH_F(w_times(W, V, d, r, omega, Y, w, s));
   LRH_F(orth(Y, Yt, V, r, w, s));
   for (int it = 0; it < q; ++it) {
     LRH_F(wt_times(W, V, d, r, Y, Z, w, s));
     LRH_F(orth(Z, Zt, d, r, w, s));
-    LRH_F((gemm<uint16_t, false, float>(W, d, Z, r, Y, (int)V, r, d, 1, s)));
+    LRH_F(w_times(W, V, d, r, Z, Y, w, s));
     LRH_F(orth(Y, Yt, V, r, w, s));
   }
   // P = Y, Q = (W^T . Y)^T

@@ -1075,6 +1075,20 @@ hipError_t launch_down_gemm(const void* Q, const void* H, int r, int d, int64_t 
   return launch_down_reduce(part, split, B * r, Z, stream);
 }
 
+hipError_t launch_gemm_f32(const uint16_t* M, int64_t Mrows, int K, const uint16_t* X, int64_t Xrows, float* S,
+                           int ksplit, hipStream_t stream) {
+  if (Mrows < 1 || Xrows < 1 || K < 8 || K % 8 || ksplit < 1) return hipErrorInvalidValue;
+  auto go = [&](auto cfg) {
+    using C = decltype(cfg);
+    const int nvb = (int)((Mrows + C::BM - 1) / C::BM);
+    return run_gemm<C>(kModePartial, M, X, Mrows, K, Xrows, nvb, 1, nullptr, 0, nullptr, S, Mrows, nullptr, 0,
+                       stream, {}, ksplit);
+  };
+  if (Xrows > 128) return go(CfgBig{});
+  if (Xrows > 64) return go(CfgWide{});
+  return go(CfgNarrow{});
+}
+
 BatchPlan plan_batch(int64_t V, int64_t B, int k) {
   BatchPlan p;
   p.nvb = vblocks(V);

@@ -153,6 +153,12 @@ size_t batch_scratch_bytes(int64_t V, int64_t B_max);
 BatchScratch batch_scratch(void* base, int64_t V, int64_t B_max);
 // Lets the GEMM kernels use more than 64 KiB of LDS (call once per device).
 hipError_t batch_init();
+// fp32 products on the GEMM kernel: S[s][n][m] = sum over the s-th of
+// `ksplit` shares of K of X[n][k] M[m][k] (M: Mrows x K, X: Xrows x K, bf16,
+// K a multiple of 8; S: ksplit x Xrows x Mrows fp32). Call batch_init()
+// once per device first.
+hipError_t launch_gemm_f32(const uint16_t* M, int64_t Mrows, int K, const uint16_t* X, int64_t Xrows, float* S,
+                           int ksplit, hipStream_t stream);
 // z = round_bf16(Q . h) for B rows on the GEMM kernel (bf16 only). With
 // too few output tiles to fill the GPU, K is split over blocks (about 512 of
 // them) whose fp32 partial sums go to `part` (when part_bytes holds them)

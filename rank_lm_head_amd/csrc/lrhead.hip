@@ -490,6 +490,7 @@ int lrhead_factor(const void* W, int64_t V, int64_t d, int r, int q, const float
     return fail(LRHEAD_EALIGN, "W, omega, P, Q and workspace must be 16-byte aligned");
   const size_t need = lrh::factor_workspace_bytes(V, d, r);
   if (workspace_bytes < need) return fail(LRHEAD_EWORKSPACE, "workspace holds %zu bytes, needs %zu", workspace_bytes, need);
+  LRH_HIP(lrh::batch_init(), "GEMM kernel set-up");   // the W-sized products run on the GEMM kernel
   LRH_HIP(lrh::launch_factor(W, V, d, r, q, omega, P, Q, workspace, static_cast<hipStream_t>(stream)),
           "factor launch");
   return LRHEAD_OK;

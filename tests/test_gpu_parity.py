@@ -565,8 +565,10 @@ def check_factor_close(P_g, Q_g, P_o, Q_o):
     (3000, 256, 32, 1),     # ragged tiles in V
     (20000, 1024, 64, 2),   # two iterations
     (4096, 200, 8, 0),      # no iteration, d not a multiple of 64
-    (9000, 1000, 128, 1),   # r >= 128: the 128 x 128-tile products; ragged tiles in V and d
+    (9000, 1000, 128, 1),   # r >= 128: 256-row GEMM tiles of the panel halves; ragged tiles in V and d
     (6000, 512, 256, 1),    # two tiles of r
+    (3001, 256, 32, 1),     # V not a multiple of 8: the W products on the vector ALU
+    (2000, 260, 64, 1),     # d not a multiple of 8: the W products on the vector ALU
 ])
 def test_factor_matches_the_oracle(V, d, r, q):
     from oracle import factor as fa
