@@ -412,7 +412,19 @@ struct CollectWave {
   int li[2][kWave];
 };
 
-template <int TM>
+// The vocabulary row of bit b of a row's 32-bit mask word w. A slice word
+// s covers lane group g = s & 3 of the TM-row block s >> 2: its bit i * 4 + q
+// stands for row (s >> 2) * TM + i * 16 + 4 g + q. Without HALF word w is
+// slice word w; with HALF it holds the 16-bit slice words 2 w (low half)
+// and 2 w + 1 (high half).
+template <int TM, bool HALF>
+__device__ __forceinline__ int mask_row(int w, int b) {
+  const int s = HALF ? 2 * w + (b >> 4) : w;
+  const int bb = HALF ? b & 15 : b;
+  return (s >> 2) * TM + (bb >> 2) * 16 + 4 * (s & 3) + (bb & 3);
+}
+
+template <int TM, bool HALF>
 __device__ __forceinline__ void collect_rounds(CollectWave& m, const uint32_t* __restrict__ mask, int NW,
                                                const float* __restrict__ S, int64_t ldS, int64_t row, int k,
                                                int32_t* __restrict__ idx, float* __restrict__ score) {
@@ -465,12 +477,10 @@ __device__ __forceinline__ void collect_rounds(CollectWave& m, const uint32_t* _
         for (int e = 0; e < 4; ++e) {
           uint32_t bits = wd[t][e];
           const int w = 4 * (lane + kWave * (c * T4 + t)) + e;
-          const int64_t slice = w >> 2, gq = w & 3;
           while (bits) {
             const int b = __builtin_ctz(bits);
             bits &= bits - 1;
-            if (pos >= base && pos < base + kColCap)
-              m.vid[pos - base] = (int)(slice * TM + (b >> 2) * 16 + 4 * gq + (b & 3));
+            if (pos >= base && pos < base + kColCap) m.vid[pos - base] = mask_row<TM, HALF>(w, b);
             ++pos;
           }
         }
@@ -519,7 +529,7 @@ __device__ __forceinline__ void collect_rounds(CollectWave& m, const uint32_t* _
 }
 
 
-template <int TM, int T4>
+template <int TM, int T4, bool HALF>
 __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* __restrict__ mask, int NW,
                                                                 const float* __restrict__ S, int64_t ldS, int64_t B,
                                                                 int k, int32_t* __restrict__ idx,
@@ -570,11 +580,10 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
       for (int e = 0; e < 4; ++e) {
         uint32_t bits = wd[t][e];
         const int w = 4 * (qb + t * kWave + lane) + e;
-        const int64_t slice = w >> 2, gq = w & 3;
         while (bits) {
           const int b = __builtin_ctz(bits);
           bits &= bits - 1;
-          if (pos < kColCap) m.vid[pos] = (int)(slice * TM + (b >> 2) * 16 + 4 * gq + (b & 3));
+          if (pos < kColCap) m.vid[pos] = mask_row<TM, HALF>(w, b);
           ++pos;
         }
       }
@@ -605,7 +614,7 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
   if (wave != 0) return;
   const int C = n_flag;
   if (C > kColCap) {
-    collect_rounds<TM>(m, mask, NW, S, ldS, row, k, idx, score);
+    collect_rounds<TM, HALF>(m, mask, NW, S, ldS, row, k, idx, score);
     return;
   }
   uint64_t key[kColE];
@@ -649,9 +658,10 @@ __global__ void __launch_bounds__(kGemmThreads) collect_kernel(const uint32_t* _
 //  kModeMax:    tile maxima, row n at aux_f + n * ns_tiles, index s * 8 +
 //               w * 2 + i2 for the 32-row tile i2 of wave w;
 //  kModeFilter: per-row bound theta; flagged scores into S (row n at
-//               S + n * ldS) and one mask word per (row, 64-row slice,
-//               lane group): word (vb * 4 + w) * 4 + g holds bit i * 4 + q
-//               for vocabulary row (vb * 4 + w) * 64 + i * 16 + 4 * g + q.
+//               S + n * ldS) and one 16-bit mask word per (row, 64-row
+//               slice, lane group): 16-bit word (vb * 4 + w) * 4 + g of row
+//               n (rows 2 NW such words apart) holds bit i * 4 + q for
+//               vocabulary row (vb * 4 + w) * 64 + i * 16 + 4 * g + q.
 constexpr int kStripRows = 256;
 
 template <int BN, int KT, int MODE>
@@ -831,7 +841,7 @@ __global__ void __launch_bounds__(kGemmThreads) strip_sel_kernel(
           for (int q = 0; q < 4; ++q) bits |= (acc[i][jn][q] >= th ? 1u : 0u) << (i * 4 + q);
         bits &= valid;
         if (n >= B) continue;
-        mask[n * NW + (vb * 4 + wave) * 4 + g] = bits;
+        reinterpret_cast<uint16_t*>(mask)[n * 2 * NW + (vb * 4 + wave) * 4 + g] = (uint16_t)bits;
         if (bits == 0) continue;
         float* srow = S + n * ldS + vrow;
 #pragma unroll
@@ -905,16 +915,17 @@ hipError_t run_gemm(int mode, const uint16_t* M, const uint16_t* X, int64_t V, i
   return hipGetLastError();
 }
 
-// One block per row; the width of the mask rounds by batch size.
-template <int TM>
+// One block per row; the width of the mask rounds by batch size. NW counts
+// 32-bit words per row; HALF: each holds two 16-bit slice words.
+template <int TM, bool HALF = false>
 hipError_t launch_collect(const uint32_t* mask, int NW, const float* S, int64_t ldS, int64_t B, int k, int32_t* idx,
                           float* score, hipStream_t stream) {
   if (B <= 1024)
-    hipLaunchKernelGGL((collect_kernel<TM, 12>), dim3((unsigned)B), dim3(kGemmThreads), 0, stream, mask, NW, S, ldS,
-                       B, k, idx, score);
+    hipLaunchKernelGGL((collect_kernel<TM, 12, HALF>), dim3((unsigned)B), dim3(kGemmThreads), 0, stream, mask, NW, S,
+                       ldS, B, k, idx, score);
   else
-    hipLaunchKernelGGL((collect_kernel<TM, 4>), dim3((unsigned)B), dim3(kGemmThreads), 0, stream, mask, NW, S, ldS,
-                       B, k, idx, score);
+    hipLaunchKernelGGL((collect_kernel<TM, 4, HALF>), dim3((unsigned)B), dim3(kGemmThreads), 0, stream, mask, NW, S,
+                       ldS, B, k, idx, score);
   return hipGetLastError();
 }
 
@@ -1003,7 +1014,7 @@ hipError_t strip_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, 
                       const BatchScratch& w, int32_t* idx, float* score, hipStream_t stream, Timing t) {
   const int NT = (int)((B + BN - 1) / BN);
   const size_t lds = strip_lds_bytes<BN, KT>();
-  const int NW = (int)(p.nvb * (kGemmBM / 64) * 4);   // 64-row mask slices
+  const int NW = (int)(p.nvb * (kGemmBM / 64) * 4 / 2);   // 64-row mask slices, two 16-bit words in 32 bits
   const int Gs = strip_groups(p.ns, NT, strip_slots<BN, KT, kModeMax>());
   hipLaunchKernelGGL((strip_sel_kernel<BN, KT, kModeMax>), dim3((unsigned)(Gs * NT)), dim3(kGemmThreads), lds,
                      stream, M, X, V, K, B, p.ns, p.stride, Gs, w.tmax, p.ns_tiles, nullptr, nullptr, 0, nullptr, 0);
@@ -1015,7 +1026,7 @@ hipError_t strip_pass(const BatchPlan& p, const uint16_t* M, const uint16_t* X, 
   LRH_LAUNCH(t, (strip_sel_kernel<BN, KT, kModeFilter>), dim3((unsigned)(Gm * NT)), dim3(kGemmThreads), lds, stream,
              M, X, V, K, B, nvb, 1, Gm, nullptr, 0, w.theta, w.S, p.ldS, w.mask, NW);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return launch_collect<64>(w.mask, NW, w.S, p.ldS, B, k, idx, score, stream);
+  return launch_collect<64, true>(w.mask, NW, w.S, p.ldS, B, k, idx, score, stream);
 }
 
 template <int KT>

@@ -229,7 +229,7 @@ def test_batch_duplicate_rows_tie_to_the_lower_id():
     assert len(set(np_(score)[0].tolist())) == 1
 
 
-@pytest.mark.parametrize("B", [1, 8, 16, 64])
+@pytest.mark.parametrize("B", [1, 8, 16, 64, 300])
 def test_all_scores_tied(B):
     """Every score equal: the k lowest ids win, in order (forces the merge's
     exhaustive path, since every entry reaches the sampled threshold)."""
@@ -408,7 +408,7 @@ def test_duplicate_rows_tie_to_the_lower_id():
     assert len(set(np_(flog)[0].tolist())) == 1
 
 
-@pytest.mark.parametrize("B", [1, 4, 8, 16, 40])
+@pytest.mark.parametrize("B", [1, 4, 8, 16, 40, 300])
 def test_ties_inside_one_slice_go_to_the_lower_ids(B):
     """Bitwise copies of the best low-rank row inside one vocabulary slice, at
     ids that share a lane and ids in different lanes: every tied copy must come
