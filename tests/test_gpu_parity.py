@@ -328,7 +328,7 @@ def test_config_full_head_baseline(cid):
 
 # ------------------------------------------------------ invariants on the GPU
 
-@pytest.mark.parametrize("B", [1, 4, 8, 20, 64])
+@pytest.mark.parametrize("B", [1, 4, 8, 20, 64, 300])
 def test_h_times_two_doubles_everything_bitwise(B):
     """h -> 2h is exact in bf16: z, scores and logits double bit for bit and
     the ids stay (one-row pass, LDS-staged and register-list streaming
@@ -340,6 +340,41 @@ def test_h_times_two_doubles_everything_bitwise(B):
     b = [np_(x) for x in head.draft((t["H"].float() * 2).to(torch.bfloat16), 32)]
     assert np.array_equal(a[0], b[0])
     assert np.array_equal(2 * a[1], b[1]) and np.array_equal(2 * a[2], b[2])
+
+
+@pytest.mark.parametrize("B", [1, 4, 8, 40, 300])
+def test_vocabulary_permutation_maps_the_ids(B):
+    """Rows of P and W permuted together (P2[v] = P[perm[v]]): every score
+    moves with its row, so each row's top-k scores, and the logits of the
+    tokens behind them, come out bit for bit the same, at ids that map back
+    through perm (one-row pass, LDS-staged, register-list and strip paths).
+    Equal scores come out in each call's own id order (ties resolve to the
+    lower id), and at the row's k-th score the ids may differ; the scores
+    may not."""
+    V, k = 3000, 16
+    inp = gen.make_custom(V, 256, 64, B, "bf16", seed=41)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    perm = np.random.default_rng(41).permutation(V)
+    pt = torch.from_numpy(perm).to(DEV)
+    P2, W2 = t["P"][pt].contiguous(), t["W"][pt].contiguous()
+    ha = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=k)
+    a = [np_(x) for x in ha.draft(t["H"], k)]
+    b = [np_(x) for x in lr.Head(t["Q"], P2, W2, B_max=B, k_max=k).draft(t["H"], k)]
+    mapped = perm[b[0]].astype(np.int32)
+    # the permuted call's logits are the original head's at the mapped ids
+    la = np_(ha.logits(t["H"], torch.from_numpy(mapped).to(DEV)))
+    torch.cuda.synchronize()
+    assert np.array_equal(a[1], b[1]), "top-k scores differ"
+    assert np.array_equal(la, b[2])
+    for row in range(B):
+        assert len(set(mapped[row].tolist())) == k, row
+        # equal scores inside the list hold the same ids, ordered by each
+        # call's own numbering; at the k-th score only the scores must agree
+        for v in set(a[1][row].tolist()) - {float(a[1][row, -1])}:
+            sa, sb = a[1][row] == v, b[1][row] == v
+            assert sorted(a[0][row][sa].tolist()) == sorted(mapped[row][sb].tolist()), (row, v)
+            la_of = dict(zip(a[0][row][sa].tolist(), a[2][row][sa].tolist()))
+            assert all(la_of[i] == x for i, x in zip(mapped[row][sb].tolist(), b[2][row][sb].tolist())), (row, v)
 
 
 @pytest.mark.parametrize("B", [1, 4, 8, 20, 64])
