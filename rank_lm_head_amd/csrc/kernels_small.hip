@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(kSmallThreads) select_short_kernel(
 
 // ------------------------------------------- score pass, 5 to 64 rows
 // The matrix-core stream (stream_mfma_tiles) with NB/16 column tiles of z
-// (z's fragments in registers, or in LDS above 64 VGPRs of them), and no
+// (z's fragments in registers, or in LDS from 64 VGPRs of them), and no
 // score leaves the registers: each lane keeps, for each of its rows
 // of z (16 c + (l & 15) in column tile c), the 4 best of the vocabulary rows
 // it is handed (rows 4 (l >> 4) .. +3 of every 16-row tile of its wave's
@@ -200,14 +200,16 @@ struct RowsLds {
   int li[kWavesSmall][4][kSliceList][kRow];
 };
 
-// z's fragments for NT column tiles take NT * K / 8 VGPRs; above 64 of them
+// z's fragments for NT column tiles take NT * K / 8 VGPRs; from 64 of them
 // (more rows of z at a larger rank) the block keeps z in LDS instead (chunk
 // j of row b at b * K/8 + (j ^ (b & 15)), so that the 16 rows a fragment
 // read touches sit on different banks) and reads each fragment just before
-// its matrix-core step. The copy shares its LDS with the lists at the end.
+// its matrix-core step: every wave loading z from L2 on its own cost more
+// at 64 VGPRs (1 us a launch at 16 x 512, 32 x 256 and 64 x 128). The copy
+// shares its LDS with the lists at the end.
 template <int K, int NB>
 constexpr bool rows_z_in_lds() {
-  return NB * K > 16 * 512;
+  return NB * K >= 16 * 512;
 }
 
 template <int K, int NB>
@@ -477,7 +479,7 @@ static int row_loads(int K) {
 int small_list_len(int k) { return k < kSliceList ? k : kSliceList; }
 
 // 5 to 64 rows: column tiles of 16, 32 or 64 rows of z, their fragments in
-// registers up to 64 VGPRs, else in LDS.
+// registers below 64 VGPRs, else in LDS.
 bool rows_path(int dtype, int64_t B, int64_t K_lowrank, int64_t V) {
   if (dtype != 0 || B < kRowsMinB || B > kRowsMaxB) return false;
   if (V > (int64_t)kMaxSmallBlocks * kBlockRows) return false;

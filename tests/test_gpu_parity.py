@@ -134,7 +134,7 @@ def test_streaming_path_shapes(V, d, r, B, k):
     (5000, 512, 256, 512, 64),   # z on the GEMM kernel, full tiles
     (40000, 256, 256, 600, 64),  # strip kernel: three batch tiles, strip groups on the XCDs, ragged last strip
     (7000, 5128, 64, 100, 32),   # split down-projection: 11 K parts, the last one 8 columns wide
-    (30000, 5120, 512, 8, 64),   # eight rows at r = 512 (register-list pass, z in registers)
+    (30000, 5120, 512, 8, 64),   # eight rows at r = 512 (register-list pass, z in LDS)
     (100, 64, 16, 300, 8),       # strip kernel: one partial strip (V < 256), two batch tiles
     (3000, 64, 8, 300, 16),      # strip kernel at r = 8: K steps mostly past the row, zero z chunks
     (3000, 1000, 128, 600, 16),  # z on the GEMM kernel split over K (4 parts), the last K stage partial
@@ -161,9 +161,11 @@ def test_batch_path_shapes(V, d, r, B, k):
     (1000, 136, 32, 12, 5),      # ragged last 16-row tile of every wave
     (300, 1032, 32, 20, 3),      # k < 4: lists of 3
     (12345, 200, 64, 33, 10),    # 64-row column tiles at r = 64, 31 idle rows
-    (20000, 512, 256, 32, 40),   # 32-row column tiles at r = 256
-    (30000, 512, 512, 16, 64),   # r = 512 on one column tile
-    (6000, 384, 128, 64, 64),    # 64 rows at r = 128, k = 64
+    (20000, 512, 256, 32, 40),   # z in LDS: 32-row column tiles at r = 256
+    (30000, 512, 512, 16, 64),   # z in LDS: r = 512 on one column tile
+    (6000, 384, 128, 64, 64),    # z in LDS: 64 rows at r = 128, k = 64
+    (20000, 512, 256, 12, 32),   # z in registers at r = 256 (one column tile)
+    (9000, 256, 128, 30, 32),    # z in registers at r = 128 (32-row column tiles)
     (200000, 64, 32, 40, 16),    # 391 rows per slice
     (20000, 512, 256, 64, 32),   # z in LDS: 64 rows at r = 256
     (5000, 256, 512, 24, 64),    # z in LDS: 32-row column tiles at r = 512
