@@ -162,6 +162,7 @@ hipError_t launch_rescore(int dtype, const void* W, const void* H, const int32_t
 }
 
 constexpr int kMergeRowBlocks = 4;
+constexpr int64_t kMergeGridBlocks = 256;
 
 hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n, int L, bool rowmajor,
                         const float* raw, const void* P, const void* Z, int K, int64_t V, int64_t B, int k,
@@ -180,12 +181,14 @@ hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n
     return hipGetLastError();
   }
   // speculative: enough blocks that waves 1..7 of all of them can hold 2k
-  // candidates; otherwise up to four blocks per row, each ranking the row's
-  // lists and rescoring its share of the winners, one per wave at a time
-  // (four measured best: 19.5 against 25.3 us at 64 rows, r = 128, k = 64,
-  // with eight blocks; 14.8 against 20.3 at k = 48)
+  // candidates; otherwise one winner per wave, in up to eight blocks per
+  // row while the grid stays within 256 blocks, else up to four (each
+  // block ranks the row's lists; at r = 128, k = 64: 18.6 against 23.9 us
+  // with six blocks at 48 rows, 19.5 against 25.3 with eight at 64 rows,
+  // but 9.8 against 11.2 with eight rather than four at 16 rows)
+  const int cap = B * 2 * kMergeRowBlocks <= kMergeGridBlocks ? 2 * kMergeRowBlocks : kMergeRowBlocks;
   const int G = speculate ? (2 * k + kMergeWaves - 2) / (kMergeWaves - 1)
-                          : min(kMergeRowBlocks, (k + kMergeWaves - 1) / kMergeWaves);
+                          : min(cap, (k + kMergeWaves - 1) / kMergeWaves);
   const dim3 grid((unsigned)G, (unsigned)B);
   if (dtype == 0)
     hipLaunchKernelGGL((merge_kernel<uint16_t, true>), grid, block, 0, stream, part_s, part_i, n, L, bl, sp, raw, Pm, Zm,
