@@ -165,6 +165,7 @@ def test_batch_path_shapes(V, d, r, B, k):
     (30000, 512, 512, 16, 64),   # z in LDS: r = 512 on one column tile
     (6000, 384, 128, 64, 64),    # z in LDS: 64 rows at r = 128, k = 64
     (20000, 512, 256, 12, 32),   # z in registers at r = 256 (one column tile)
+    (8000, 264, 64, 57, 20),     # two rows of Q per down-projection block, last group of h 1 row
     (9000, 256, 128, 30, 32),    # z in registers at r = 128 (32-row column tiles)
     (200000, 64, 32, 40, 16),    # 391 rows per slice
     (20000, 512, 256, 64, 32),   # z in LDS: 64 rows at r = 256
