@@ -650,7 +650,7 @@ def main() -> int:
     one_row = cfg.dtype == "bf16" and cfg.B == 1 and pow2_r and (cfg.V + n_b1 - 1) // n_b1 <= B1_MAX_ROWS_PER_BLOCK
     rows = cfg.dtype == "bf16" and 5 <= cfg.B <= 64 and cfg.r in (32, 64, 128, 256, 512) and cfg.V <= 512 * 512
     batch = cfg.dtype == "bf16" and cfg.B > 4 and not small and not rows
-    if batch and cfg.r <= 256 and cfg.B > 256:
+    if batch and cfg.r <= 256 and cfg.B > 128:
         sel_kernel, what = "strip_sel_kernel", "main pass: scores of all rows, flagged above the sampled bound"
     elif batch:
         sel_kernel, what = "gemm_sel_kernel", "main GEMM pass: scores of all rows, flagged above the sampled bound"

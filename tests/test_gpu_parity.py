@@ -136,6 +136,8 @@ def test_streaming_path_shapes(V, d, r, B, k):
     (7000, 5128, 64, 100, 32),   # split down-projection: 11 K parts, the last one 8 columns wide
     (30000, 5120, 512, 8, 64),   # eight rows at r = 512 (register-list pass, z in LDS)
     (100, 64, 16, 300, 8),       # strip kernel: one partial strip (V < 256), two batch tiles
+    (20000, 256, 128, 200, 32),  # strip kernel with one batch tile (129-256 rows), strips spread evenly
+    (5000, 128, 64, 129, 16),    # strip kernel at its lowest row count, 127 idle rows in the tile
     (3000, 64, 8, 300, 16),      # strip kernel at r = 8: K steps mostly past the row, zero z chunks
     (3000, 1000, 128, 600, 16),  # z on the GEMM kernel split over K (4 parts), the last K stage partial
 ])
