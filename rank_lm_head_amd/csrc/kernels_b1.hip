@@ -9,9 +9,9 @@
 // that stream is latency, and this file cuts it to two launches:
 //
 //   down_wide_kernel  z = Q . h for up to 64 rows, one block per row of Q
-//                     (two above 48 rows) and group of 8 rows (each reading
-//                     whole rows of Q at once), and the reset of the one-row
-//                     pass's completion counters.
+//                     (two above 48 rows at r <= 256) and group of 8 rows
+//                     (each reading whole rows of Q at once), and the reset
+//                     of the one-row pass's completion counters.
 //   draft1_kernel     one block per compute unit streams its vocabulary
 //                     slice of P, takes the slice's best L = min(4, k)
 //                     entries and, speculatively, the exact logit of the
@@ -556,9 +556,10 @@ hipError_t launch_down_wide(const void* Q, const void* H, int r, int d, int64_t 
   if (B < 1 || B > kDownWideMaxB || nsync > kDownThreads || n_lgs < 0) return hipErrorInvalidValue;
   uint32_t* lg32 = reinterpret_cast<uint32_t*>(lgs);
   const int groups = (int)((B + kSmallB - 1) / kSmallB);
-  // rows of Q per block: two above 48 rows of h (8.0 -> 7.4 us at 64 rows,
-  // r = 128; slower at 48 and below, where fewer blocks hide less latency)
-  const int nq = B > 48 ? 2 : 1;
+  // rows of Q per block: two above 48 rows of h at r <= 256 (8.0 -> 7.4 us
+  // at 64 rows, r = 128; 12.6 -> 12.3 at r = 256; slower at 48 rows and
+  // below, and at r = 512: 19.6 -> 22.2)
+  const int nq = B > 48 && r <= 256 ? 2 : 1;
   const dim3 grid((unsigned)((r + nq - 1) / nq), (unsigned)groups), block(kDownThreads);
   const int nl = down_wide_loads(d);
   const uint16_t* q = (const uint16_t*)Q;

@@ -64,7 +64,7 @@ hipError_t launch_select_rows(const void* M, const void* X, int64_t V, int K, in
 
 // ------------------------------------------------------- kernels_b1.hip
 // z = round(Q . h) for B <= kDownWideMaxB rows, one block per row of Q (two
-// above 48 rows) and group of 8 rows; block 0
+// above 48 rows at r <= 256) and group of 8 rows; block 0
 // also zeroes nsync completion counters (128 bytes apart) of the next pass,
 // and the blocks mark its n_lgs speculative logits "not written".
 constexpr int kDownWideMaxB = 64;
