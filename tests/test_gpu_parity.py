@@ -382,6 +382,46 @@ def test_vocabulary_permutation_maps_the_ids(B):
             assert all(la_of[i] == x for i, x in zip(mapped[row][sb].tolist(), b[2][row][sb].tolist())), (row, v)
 
 
+@pytest.mark.parametrize("B", [1, 4, 8, 64, 300])
+def test_graph_replays_match_eager_calls(B):
+    """The draft call captured in a HIP graph, as the bench times it, gives on
+    every replay the bits of the eager call on the same rows: the rows change
+    between replays, and eager calls and synchronisations run in between (one
+    row, LDS-staged, register-list and strip paths; nothing the calls need is
+    carried over in the workspace)."""
+    V, d, r, k = 20000, 512, 128, 32
+    inp = gen.make_custom(V, d, r, B, "bf16", seed=77)
+    t = {x: dev(inp[x], DEV) for x in ("Q", "P", "W", "H")}
+    H2 = dev(gen.make_custom(V, d, r, B, "bf16", seed=78)["H"], DEV)
+    head = lr.Head(t["Q"], t["P"], t["W"], B_max=B, k_max=k)
+    refs = [[np_(x) for x in head.draft(h, k)] for h in (t["H"], H2)]
+    hbuf = t["H"].clone()
+    out = (torch.empty((B, k), dtype=torch.int32, device=DEV), torch.empty((B, k), dtype=torch.float32, device=DEV),
+           torch.empty((B, k), dtype=torch.float32, device=DEV))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        head.draft(hbuf, k, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        head.draft(hbuf, k, out=out)
+    torch.cuda.synchronize()
+    for trial in range(6):
+        which = trial % 2
+        hbuf.copy_(t["H"] if which == 0 else H2)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [np_(x) for x in out]
+        for a, b in zip(refs[which], got):
+            assert np.array_equal(a, b), (trial, B)
+        # eager work of the program between replays
+        eager = [np_(x) for x in head.draft(H2 if which == 0 else t["H"], k)]
+        for a, b in zip(refs[1 - which], eager):
+            assert np.array_equal(a, b), (trial, B)
+
+
 @pytest.mark.parametrize("B", [1, 4, 8, 20, 64])
 def test_draft_logits_equal_rescoring_bitwise(B):
     """The draft call's logits (speculative per-slice rescoring and the merge's
