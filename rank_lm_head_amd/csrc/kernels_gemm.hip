@@ -865,10 +865,14 @@ constexpr int kGemmBM = 256;
 
 int64_t vblocks(int64_t V) { return (V + kGemmBM - 1) / kGemmBM; }
 
+// The sample pass reads every s-th vocabulary block: about 4 k sampled
+// 16-row tiles, at most every 7th block (at 2048 rows, r = 256, k = 64:
+// 523.3 -> 519.5 us per call against every 8th, the denser sample cutting
+// the flagged scores by more than its own cost; every 6th was no better).
 int sample_stride(int64_t V, int k) {
   const int64_t nvb = vblocks(V);
   int64_t s = nvb * (kGemmBM / 16) / (4 * (int64_t)k);
-  if (s > 8) s = 8;
+  if (s > 7) s = 7;
   if (s < 1) s = 1;
   const int64_t lo = (nvb + kMaxSampleTiles / (kGemmBM / 16) - 1) / (kMaxSampleTiles / (kGemmBM / 16));
   if (s < lo) s = lo;
