@@ -181,13 +181,19 @@ hipError_t launch_merge(int dtype, const float* part_s, const int* part_i, int n
     return hipGetLastError();
   }
   // speculative: enough blocks that waves 1..7 of all of them can hold 2k
-  // candidates; otherwise one winner per wave, in up to eight blocks per
-  // row while the grid stays within 256 blocks, else up to four (each
-  // block ranks the row's lists; at r = 128, k = 64: 18.6 against 23.9 us
-  // with six blocks at 48 rows, 19.5 against 25.3 with eight at 64 rows,
-  // but 9.8 against 11.2 with eight rather than four at 16 rows)
+  // candidates, and up to twice that while the grid stays within 256
+  // blocks (the candidates' logits spread over more waves: 6.5 -> 5.95 us
+  // at 4 rows, 7.2 -> 6.5 at 8, 7.4 -> 6.9 at 16, r = 128, k = 32; beyond
+  // 256 blocks 10.9 us at 16 rows). Otherwise one winner per wave, in up
+  // to eight blocks per row while the grid stays within 256 blocks, else
+  // up to four (each block ranks the row's lists; at r = 128, k = 64: 18.6
+  // against 23.9 us with six blocks at 48 rows, 19.5 against 25.3 with
+  // eight at 64 rows, but 9.8 against 11.2 with eight rather than four at
+  // 16 rows)
+  const int spec_min = (2 * k + kMergeWaves - 2) / (kMergeWaves - 1);
+  const int spec_max = (4 * k + kMergeWaves - 2) / (kMergeWaves - 1);
   const int cap = B * 2 * kMergeRowBlocks <= kMergeGridBlocks ? 2 * kMergeRowBlocks : kMergeRowBlocks;
-  const int G = speculate ? (2 * k + kMergeWaves - 2) / (kMergeWaves - 1)
+  const int G = speculate ? min(spec_max, max(spec_min, (int)(kMergeGridBlocks / B)))
                           : min(cap, (k + kMergeWaves - 1) / kMergeWaves);
   const dim3 grid((unsigned)G, (unsigned)B);
   if (dtype == 0)
